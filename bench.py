@@ -1,0 +1,241 @@
+"""Benchmark of the NVFP4 W4A4 quantized-linear hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: online NVFP4 quantization of the activations
+X [32768, 5120] (bf16, heavy-tailed synthetic data) followed by the fused Gated DeltaNet input
+projection GEMM against six separately calibrated NVFP4 weight segments (q 2048, k 2048, v 4096,
+z 4096, b 32, a 32; N = 12352), with per-segment global scales, bf16 outputs for q/k/v/z, the
+sigmoid gate for b and the decay gate for a (FP32). Weights are quantized once, before timing, as
+they would be offline; the activation global scale is a static calibration input, also set up
+before timing. Inputs are resident in HBM when the timed region starts.
+
+Prints one JSON line. `value` is the step's throughput in GEMM TFLOP/s (2 M N K per step time);
+`roofline` describes the dominant kernel (the GEMM) against the dense FP16 MFMA peak it runs on;
+`roofline_quantize` the quantizer against HBM bandwidth; `cpu_baseline` the CPU oracle on a bounded
+sample of the same step, extrapolated linearly in M.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import nvfp4_w4a4_quantized_quantize_amd as nv  # noqa: E402
+import workloads as wl  # noqa: E402
+
+PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0  # read bf16, write codes + scales
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class Step:
+    """Device buffers and the launches of one step of the fused GDN input projection."""
+
+    def __init__(self, case: wl.GemmCase, seed: int = 0):
+        self.case = case
+        M, K, N = case.M, case.K, case.N
+        dev = torch.device("cuda")
+        t0 = time.time()
+        self.x_bits = wl.draw_x(case, seed)
+        self.x = to_dev_bf16(self.x_bits)
+        log(f"[setup] X {self.x_bits.shape} drawn and uploaded in {time.time() - t0:.1f}s")
+        # offline: weights per segment -> global scale -> NVFP4, concatenated along N
+        self.w_codes, self.w_scales = nv.alloc_nvfp4(N, K, dev)
+        self.g_w, self.w_bits = [], []
+        n0 = 0
+        for s, seg in enumerate(case.segments):
+            wb = wl.draw_w(case, s, seed)
+            self.w_bits.append(wb)
+            wt = to_dev_bf16(wb)
+            g = float(nv.global_scale(wt).item())
+            nv.quantize(wt, g, self.w_codes[n0:n0 + seg.n], self.w_scales[n0:n0 + seg.n])
+            self.g_w.append(g)
+            n0 += seg.n
+        # static activation calibration
+        self.g_a = float(nv.global_scale(self.x).item())
+        self.a_codes, self.a_scales = nv.alloc_nvfp4(M, K, dev)
+        self.segments = []
+        for s, seg in enumerate(case.segments):
+            dt = torch.float32 if seg.out_dtype == wl.OUT_F32 else torch.bfloat16
+            epi = {wl.EPI_NONE: "none", wl.EPI_SIGMOID: "sigmoid", wl.EPI_GDN_DECAY: "gdn_decay"}[seg.epilogue]
+            a_log = dt_bias = None
+            if seg.epilogue == wl.EPI_GDN_DECAY:
+                al, db = wl.draw_gate_params(case, s, seed)
+                a_log, dt_bias = torch.from_numpy(al).cuda(), torch.from_numpy(db).cuda()
+            out = torch.empty((M, seg.n), dtype=dt, device=dev)
+            self.segments.append(nv.Segment(seg.n, self.g_w[s], epi, dt, a_log, dt_bias, out))
+        torch.cuda.synchronize()
+        log(f"[setup] weights quantized, g_a = {self.g_a:.6g}, setup {time.time() - t0:.1f}s")
+
+    def quantize(self):
+        nv.quantize(self.x, self.g_a, self.a_codes, self.a_scales)
+
+    def gemm(self):
+        nv.gemm(self.a_codes, self.a_scales, self.g_a, self.w_codes, self.w_scales, self.segments)
+
+
+def run_gpu(step: Step, steps: int, warmup: int) -> dict:
+    for _ in range(warmup):
+        step.quantize()
+        step.gemm()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()  # the library launches on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step.quantize()
+        ev[i][1].record(stream)
+        step.gemm()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    g_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    return {"wall_s": wall, "step_ms": total_ms / steps, "quant_ms": float(np.mean(q_ms)),
+            "gemm_ms": float(np.mean(g_ms)), "quant_ms_med": float(np.median(q_ms)),
+            "gemm_ms_med": float(np.median(g_ms))}
+
+
+def run_cpu_baseline(step: Step, rows_quant: int, rows_gemm: int) -> dict:
+    """The CPU oracle on a bounded sample of the same step, extrapolated linearly in M."""
+    import oracle
+    case = step.case
+    M, N, K = case.M, case.N, case.K
+    # oracle-side operands: weights quantized by the oracle itself (offline, untimed)
+    wq = [oracle.quantize(wb, oracle.global_scale(wb)) for wb in step.w_bits]
+    w_codes = np.concatenate([c for c, _ in wq])
+    w_scales = np.concatenate([s for _, s in wq])
+    g_w = np.array([oracle.global_scale(wb) for wb in step.w_bits], np.float32)
+    g_a = oracle.global_scale(step.x_bits)
+    bounds = case.seg_bounds
+    xs = step.x_bits[:rows_quant]
+    t0 = time.perf_counter()
+    a_codes, a_scales = oracle.quantize(xs, g_a)
+    t_quant = time.perf_counter() - t0
+    rows = np.arange(rows_gemm)
+    t0 = time.perf_counter()
+    oracle.gemm_rows(a_codes, a_scales, g_a, w_codes, w_scales, bounds, g_w, rows[:1])
+    t_one = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    y, T = oracle.gemm_rows(a_codes, a_scales, g_a, w_codes, w_scales, bounds, g_w, rows)
+    t_many = time.perf_counter() - t0
+    per_row = max(t_many - t_one, 1e-9) / max(rows_gemm - 1, 1)
+    fixed = max(t_one - per_row, 0.0)
+    t_full = t_quant / rows_quant * M + fixed + per_row * M
+    # sanity: the timed GPU step's outputs on the sampled rows against the oracle (FP32 segments)
+    checks = {}
+    for s, seg in enumerate(step.segments):
+        lo, hi = bounds[s], bounds[s + 1]
+        got = step.segments[s].out[:rows_gemm].float().cpu().numpy().astype(np.float64)
+        ys, Ts = y[:, lo:hi], T[:, lo:hi]
+        if seg.epilogue == "none":
+            tol = 2.0 ** -20 * Ts + (2.0 ** -8 * (np.abs(ys) + 2.0 ** -20 * Ts) if seg.out_dtype == torch.bfloat16 else 0)
+            checks[case.segments[s].name] = bool((np.abs(got - ys) <= tol).all())
+        elif seg.epilogue == "sigmoid":
+            b = oracle.sigmoid(ys)
+            checks[case.segments[s].name] = bool((np.abs(got - b) <= b * (1 - b) * 2.0 ** -20 * Ts + 2.0 ** -20 * b + 2.0 ** -126).all())
+        else:
+            al = seg.A_log.cpu().numpy()
+            db = seg.dt_bias.cpu().numpy()
+            a = oracle.gdn_decay(ys, al, db)
+            sig = 1 / (1 + np.exp(-(ys + db.astype(np.float64))))
+            bound = a * np.exp(al.astype(np.float64)) * sig * 2.0 ** -20 * Ts + 2.0 ** -20 * a * (1 + np.abs(np.log(np.maximum(a, 1e-300)))) + 2.0 ** -126
+            checks[case.segments[s].name] = bool((np.abs(got - a) <= bound).all())
+    codes_ok = bool((step.a_codes[:rows_quant].cpu().numpy() == a_codes).all()
+                    and (step.a_scales[:rows_quant].cpu().numpy() == a_scales).all())
+    return {
+        "value": 2.0 * M * N * K / t_full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"oracle quantize of {rows_quant} rows + exact GEMM of {rows_gemm} rows (all N) of the "
+                   f"{M}x{N}x{K} step, extrapolated linearly to M={M}; measured "
+                   f"{t_quant:.2f}s + {t_many:.2f}s, extrapolated full step {t_full:.1f}s"),
+        "parity_sample": {"codes_scales_bit_exact": codes_ok, **checks},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C5", choices=sorted(wl.ALL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-quant", type=int, default=32768)
+    ap.add_argument("--cpu-rows-gemm", type=int, default=4096)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the hot path has no multi-GPU part here (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    nv.lib()  # fail loudly if the HIP library is missing
+    case = wl.ALL[args.workload]
+    step = Step(case)
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log(f"[gpu] warmup {args.warmup}, timing {args.steps} steps")
+    r = run_gpu(step, args.steps, args.warmup)
+    M, N, K = case.M, case.N, case.K
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (r["gemm_ms"] * 1e-3) / 1e12
+    q_bytes = QUANT_BYTES_PER_ELEM * M * K
+    q_gbps = q_bytes / (r["quant_ms"] * 1e-3) / 1e9
+    log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {r['quant_ms']:.3f} ms ({q_gbps:.0f} GB/s), "
+        f"gemm {r['gemm_ms']:.3f} ms ({gemm_tflops:.0f} TFLOP/s)")
+    out = {
+        "metric": "NVFP4 W4A4 GEMM TFLOPS at 32K-token prefill + quantize GB/s, % of roofline",
+        "value": flops / (r["step_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["step_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 MFMA operands (exact NVFP4 decode), f32 accumulate",
+        "data": "synthetic (seeded; heavy-tailed activations with outlier channels, per-segment weight spreads)",
+        "config": {"workload": case.name, "M": M, "N": N, "K": K,
+                   "segments": ",".join(f"{s.name}{s.n}" for s in case.segments),
+                   "epilogues": "q,k,v,z bf16; b sigmoid f32; a gdn_decay f32"},
+        "gemm_tflops": gemm_tflops,
+        "quantize_gbps": q_gbps,
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / PEAK_F16_MFMA_TFLOPS, "traffic": None,
+                     "kernel": "gemm_kernel", "avg_ms": r["gemm_ms"], "algorithmic_flop": flops},
+        "roofline_quantize": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                              "frac": q_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quantize_kernel",
+                              "avg_ms": r["quant_ms"], "algorithmic_bytes": q_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[cpu] timing the oracle on a sample")
+        out["cpu_baseline"] = run_cpu_baseline(step, args.cpu_rows_quant, args.cpu_rows_gemm)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

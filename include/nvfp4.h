@@ -1,0 +1,156 @@
+/*
+ * nvfp4.h -- C interface of the MI355X (gfx950) NVFP4 W4A4 quantized-linear library (libnvfp4.so).
+ *
+ * The library implements the data-parallel hot path of an all-linear-layers NVFP4 W4A4 recipe
+ * (paper arXiv:2609.04098, "Why Gated DeltaNet Survives 4-Bit Quantization"):
+ *
+ *   1. online activation quantization to NVFP4: E2M1 4-bit elements, one E4M3 scale per 16
+ *      consecutive elements along K chosen from the block maximum, and one FP32 global scale per
+ *      linear module (Japanese article, "Mechanism 1" and FAQ "What is NVFP4?"; English abstract,
+ *      point (i));
+ *   2. the block-scaled W4A4 GEMM Y = X W^T with FP32 accumulation, where one GEMM may serve several
+ *      separately calibrated modules fused along N, each output-column segment applying its own
+ *      global scale after accumulation -- the repair of the fused-module global-scale mismatch
+ *      (Japanese article, "Trap 1"; English abstract; aimodeling.com English translation, "What
+ *      engineers should actually take away"), with an optional Gated DeltaNet gate epilogue
+ *      (Japanese article, "Mechanism 2").
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers; `stream` is a hipStream_t passed as void* (NULL means
+ *    the null stream). Work is enqueued on `stream` and the call returns without synchronizing.
+ *  - The caller owns every buffer. The library never allocates, frees or synchronizes device
+ *    memory. Device buffers must stay valid until the stream has executed the work.
+ *  - Host arrays (segment tables, scale vectors) are read only during the call.
+ *  - Argument errors are returned synchronously before anything is enqueued; a failed launch
+ *    returns NVFP4_ERR_HIP. nvfp4_last_error() then gives a thread-local description.
+ *  - Results are bitwise deterministic for identical inputs and shapes (no floating-point atomics).
+ *  - No exceptions cross this interface. Calls from several host threads are safe.
+ *
+ * Data layouts (row-major; all strides are in ELEMENTS of the buffer's own type, i.e. bytes for the
+ * uint8 code/scale buffers)
+ *  - bf16 activations X [rows, K], row stride ldx >= K.
+ *  - NVFP4 tensor = codes [rows, K/2] uint8 + scales [rows, K/16] uint8:
+ *      codes byte j of a row holds element 2j in bits 0-3 and element 2j+1 in bits 4-7;
+ *      a 4-bit code is sign (bit 3) | E2M1 magnitude (bits 2-0) with magnitudes
+ *      {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *      scales byte b of a row is the OCP E4M3FN scale of elements [16b, 16b+16), never negative;
+ *      decoded value x ~= e2m1(code) * e4m3(scale) * g, with g the tensor's FP32 global scale.
+ *    Weights use the same layout with rows = N (as nn.Linear: W [N, K], Y = X W^T).
+ *  - Alignment: every base pointer is 16-byte aligned and every row stride is a multiple of 16
+ *    bytes (ldx a multiple of 8 elements; ldc and lds multiples of 16). A buffer of R rows holds
+ *    at least R * stride bytes. Violations return NVFP4_ERR_ALIGN; there is no slow fallback.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,     /* negative size, K not a multiple of 16, stride smaller than a row */
+    NVFP4_ERR_ALIGN = 3,     /* pointer or stride misaligned (see "Alignment" above) */
+    NVFP4_ERR_SEGMENTS = 4,  /* segment table empty, too long, unsorted, overlapping or not covering N */
+    NVFP4_ERR_SCALE = 5,     /* a global scale is not finite and > 0 */
+    NVFP4_ERR_EPILOGUE = 6,  /* unknown epilogue/out dtype, or a gate without FP32 output/parameters */
+    NVFP4_ERR_WORKSPACE = 7, /* workspace smaller than nvfp4_gemm_workspace_bytes() */
+    NVFP4_ERR_HIP = 8        /* the HIP runtime reported an error (launch failure, bad stream) */
+} nvfp4_status;
+
+enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
+enum { NVFP4_EPI_NONE = 0, NVFP4_EPI_SIGMOID = 1, NVFP4_EPI_GDN_DECAY = 2 };
+enum { NVFP4_MAX_SEGMENTS = 16 };
+
+/*
+ * nvfp4_global_scale -- calibration of a module's FP32 global scale from a bf16 tensor:
+ *   g = RN32(amax / 2688), amax = max |x| over the tensor, 2688 = 6 * 448 (largest E2M1 magnitude
+ *   times largest E4M3 scale), so that the tensor maximum lands on the top of both grids.
+ * The pages fix one global scale per linear module by calibration ("Trap 1", "Experiment design");
+ * the synthetic workloads take it from the tensor itself. Writes one float to the device pointer
+ * g_out (which the call also uses as its reduction accumulator). rows == 0 or K == 0 gives g = 0.
+ * x: device bf16 [rows, K], stride ldx (elements). Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+nvfp4_status nvfp4_global_scale(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx,
+                                float* g_out, void* stream);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of bf16 rows (activations online; weights offline).
+ * For every 16-element block along K, with RN32 = one IEEE binary32 operation rounded to nearest
+ * even:
+ *   amax_b = max |x|;  s = E4M3_RNE_SAT(RN32(amax_b / RN32(6 g)))  (saturating at 448);
+ *   if s == 0 every magnitude is 0, else  code = signbit(x) * 8 + E2M1_RNE_SAT(RN32(|x| / RN32(s g)))
+ *   (E2M1 saturating at 6; ties to the even code; -0.0 and values rounding to zero keep their sign).
+ * Block scaling per the Japanese article, "Mechanism 1"; one FP32 global scale g per module per
+ * "Trap 1" and the English abstract.
+ *   x_bf16: device bf16 [rows, K], stride ldx elements;  g: host float, finite and > 0;
+ *   codes: device uint8 [rows, K/2], stride ldc bytes;  scales: device uint8 [rows, K/16], stride lds.
+ * K must be a multiple of 16. rows == 0 or K == 0 is a no-op.
+ * Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
+ */
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx, float g,
+                            uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                            void* stream);
+
+/*
+ * One output-column segment of a (possibly fused) GEMM: columns [n_begin, n_begin + n_len) of W,
+ * i.e. one separately calibrated linear module ("Trap 1": the fused in_proj_qkv+z and in_proj_b+a
+ * GEMMs). The segment writes its own output matrix out [M, n_len] with row stride ldo (elements):
+ *   y[m, j] = g_a * g_w[s] * sum_k a[m, k] w[n_begin + j, k]    (accumulated in FP32)
+ *   epilogue NONE:      out = y                     (out_dtype F32, or BF16 rounded to nearest even)
+ *   epilogue SIGMOID:   out = 1 / (1 + exp(-y))     (write strength beta; out_dtype must be F32)
+ *   epilogue GDN_DECAY: out = exp(-exp(A_log[j]) * softplus(y + dt_bias[j]))
+ *                       (decay alpha; out_dtype must be F32; A_log, dt_bias: device float [n_len])
+ * Gates follow the Gated DeltaNet parameterization of the Japanese article, "Mechanism 2"; their
+ * outputs are FP32 because a decay close to 1 is not representable in bf16.
+ * Several segments may share one output buffer by pointing `out` at column n_begin of it.
+ */
+typedef struct {
+    int64_t n_begin;
+    int64_t n_len;
+    int32_t epilogue;   /* NVFP4_EPI_* */
+    int32_t out_dtype;  /* NVFP4_OUT_* */
+    void* out;          /* device, [M, n_len], stride ldo elements; 16-byte aligned, ldo*size%16==0 */
+    int64_t ldo;
+    const float* A_log;   /* GDN_DECAY only, else ignored */
+    const float* dt_bias; /* GDN_DECAY only, else ignored */
+} nvfp4_segment;
+
+/*
+ * nvfp4_gemm -- block-scaled W4A4 GEMM with a per-segment global-scale epilogue.
+ *   a_codes/a_scales: device NVFP4 activations [M, K] (strides lda_c, lda_s bytes), global scale g_a;
+ *   w_codes/w_scales: device NVFP4 weights [N, K] (strides ldw_c, ldw_s bytes);
+ *   segs[n_segs]: host array, sorted by n_begin, contiguous, non-overlapping, covering [0, N),
+ *                 every n_len > 0, 1 <= n_segs <= NVFP4_MAX_SEGMENTS;
+ *   g_w[n_segs]: host array, the weight global scale of each segment (finite, > 0).
+ * The product of the decoded operands is accumulated in FP32 from exact FP16 products (an E2M1
+ * value times an E4M3 scale is exact in FP16), then scaled once by RN32(g_a * g_w[s]).
+ * M == 0 or N == 0 is a no-op; K == 0 writes the epilogue of y = 0.
+ * workspace: device scratch of at least nvfp4_gemm_workspace_bytes(M, N, K) bytes (may be NULL
+ * when that is 0).
+ * Errors: NULL, SHAPE, ALIGN, SEGMENTS, SCALE, EPILOGUE, WORKSPACE, HIP.
+ */
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
+                        int64_t lda_s, float g_a, const uint8_t* w_codes, int64_t ldw_c,
+                        const uint8_t* w_scales, int64_t ldw_s, int64_t M, int64_t N, int64_t K,
+                        const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none). */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Static English name of a status code. */
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

@@ -1,0 +1,187 @@
+"""Python binding of libnvfp4.so, the MI355X (gfx950) NVFP4 W4A4 quantized-linear library.
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels. PyTorch is
+used for device memory and the current stream. The names mirror the C interface in
+include/nvfp4.h (nvfp4_global_scale, nvfp4_quantize, nvfp4_gemm).
+
+If the library has not been built (``python -m nvfp4_w4a4_quantized_quantize_amd.build``), every
+call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+OK = 0
+OUT_F32, OUT_BF16 = 0, 1
+EPI_NONE, EPI_SIGMOID, EPI_GDN_DECAY = 0, 1, 2
+MAX_SEGMENTS = 16
+_EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
+
+# Every function the C header declares; a test checks the library exports all of them.
+EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
+            "nvfp4_status_string", "nvfp4_last_error")
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)}): {detail}")
+        self.status = status
+
+
+class _Segment(ctypes.Structure):
+    _fields_ = [("n_begin", ctypes.c_int64), ("n_len", ctypes.c_int64), ("epilogue", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4.so (raises if it is missing: the path has no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m nvfp4_w4a4_quantized_quantize_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, f32, P = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+        L.nvfp4_global_scale.restype = i32
+        L.nvfp4_global_scale.argtypes = [P, i64, i64, i64, P, P]
+        L.nvfp4_quantize.restype = i32
+        L.nvfp4_quantize.argtypes = [P, i64, i64, i64, f32, P, i64, P, i64, P]
+        L.nvfp4_gemm.restype = i32
+        L.nvfp4_gemm.argtypes = [P, i64, P, i64, f32, P, i64, P, i64, i64, i64, i64,
+                                 ctypes.POINTER(_Segment), ctypes.POINTER(f32), i32, P, ctypes.c_size_t, P]
+        L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_status_string.argtypes = [i32]
+        L.nvfp4_last_error.restype = ctypes.c_char_p
+        L.nvfp4_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().nvfp4_last_error().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Nvfp4Error(status, where, last_error())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _round16(n: int) -> int:
+    return (n + 15) // 16 * 16
+
+
+def _ld(t: torch.Tensor, multiple: int) -> int:
+    """Row stride in elements; a single-row tensor may carry any stride, so report a valid one."""
+    if t.shape[0] > 1:
+        return t.stride(0)
+    return (t.shape[1] + multiple - 1) // multiple * multiple
+
+
+def alloc_nvfp4(rows: int, K: int, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Codes [rows, K/2] and scales [rows, K/16] uint8 views with 16-byte-multiple row strides."""
+    cb = torch.empty((rows, _round16(K // 2)), dtype=torch.uint8, device=device)
+    sb = torch.empty((rows, _round16(K // 16)), dtype=torch.uint8, device=device)
+    return cb[:, :K // 2], sb[:, :K // 16]
+
+
+# --------------------------------------------------------------------------------------- a1: scale
+def global_scale(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """g = RN32(max|x| / 2688) of a bf16 [rows, K] device tensor, as a float32 device tensor [1]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_global_scale(_ptr(x), x.shape[0], x.shape[1], _ld(x, 8), _ptr(out), _stream(stream)),
+           "nvfp4_global_scale")
+    return out
+
+
+# ------------------------------------------------------------------------------------ a2-a4: quantize
+def quantize(x: torch.Tensor, g: float, codes: Optional[torch.Tensor] = None,
+             scales: Optional[torch.Tensor] = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """NVFP4-quantize a bf16 [rows, K] device tensor with FP32 global scale g.
+
+    Returns (codes uint8 [rows, K/2], scales uint8 [rows, K/16]) (preallocated ones may be passed).
+    """
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    if codes is None or scales is None:
+        codes, scales = alloc_nvfp4(rows, K, x.device)
+    _check(lib().nvfp4_quantize(_ptr(x), rows, K, _ld(x, 8), float(g), _ptr(codes), _ld(codes, 16),
+                                _ptr(scales), _ld(scales, 16), _stream(stream)), "nvfp4_quantize")
+    return codes, scales
+
+
+# ------------------------------------------------------------------------------------- a5-a7: GEMM
+@dataclasses.dataclass
+class Segment:
+    """One output-column segment (one separately calibrated module) of a fused GEMM."""
+    n: int
+    g_w: float
+    epilogue: str = "none"                 # "none", "sigmoid" or "gdn_decay"
+    out_dtype: torch.dtype = torch.float32  # torch.float32 or torch.bfloat16
+    A_log: Optional[torch.Tensor] = None    # float32 [n] device (gdn_decay)
+    dt_bias: Optional[torch.Tensor] = None  # float32 [n] device (gdn_decay)
+    out: Optional[torch.Tensor] = None      # preallocated [M, n] output (optional)
+
+
+def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: torch.Tensor,
+         w_scales: torch.Tensor, segments: Sequence[Segment], workspace: Optional[torch.Tensor] = None,
+         stream=None) -> list[torch.Tensor]:
+    """Block-scaled W4A4 GEMM Y = A W^T with one global scale per output segment.
+
+    a_codes [M, K/2], a_scales [M, K/16]; w_codes [N, K/2], w_scales [N, K/16] (uint8, device).
+    Returns one output tensor [M, n_s] per segment.
+    """
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    assert w_codes.shape[1] * 2 == K and a_scales.shape == (M, K // 16) and w_scales.shape == (N, K // 16)
+    assert sum(s.n for s in segments) == N, "segments must cover N"
+    n_segs = len(segments)
+    segs = (_Segment * max(n_segs, 1))()
+    g_w = (ctypes.c_float * max(n_segs, 1))()
+    outs = []
+    begin = 0
+    for i, s in enumerate(segments):
+        dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[s.out_dtype]
+        out = s.out if s.out is not None else torch.empty((M, s.n), dtype=s.out_dtype, device=a_codes.device)
+        assert out.dtype == s.out_dtype and out.dim() == 2 and out.stride(1) == 1
+        segs[i] = _Segment(begin, s.n, _EPI[s.epilogue], dt, _ptr(out), _ld(out, 1),
+                           _ptr(s.A_log), _ptr(s.dt_bias))
+        g_w[i] = float(s.g_w)
+        outs.append(out)
+        begin += s.n
+    need = lib().nvfp4_gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvfp4_gemm(_ptr(a_codes), _ld(a_codes, 16), _ptr(a_scales), _ld(a_scales, 16), float(g_a),
+                            _ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), M, N, K,
+                            segs, g_w, n_segs, _ptr(workspace), ws_bytes, _stream(stream)), "nvfp4_gemm")
+    return outs

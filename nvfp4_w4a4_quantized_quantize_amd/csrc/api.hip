@@ -1,0 +1,177 @@
+// C interface of libnvfp4.so: argument validation, status reporting and kernel launches.
+// Every argument error is reported before anything is enqueued on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+nvfp4_status ok() {
+    g_last_error[0] = '\0';
+    return NVFP4_OK;
+}
+
+nvfp4_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float g) { return std::isfinite(g) && g > 0.0f; }
+
+// A [rows, K] bf16 matrix with stride ldx elements.
+nvfp4_status check_bf16_matrix(const void* x, int64_t rows, int64_t K, int64_t ldx, const char* name) {
+    if (rows < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "%s: negative shape [%lld, %lld]", name, (long long)rows, (long long)K);
+    if (rows == 0 || K == 0) return NVFP4_OK;
+    if (!x) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
+    if (ldx < K) return fail(NVFP4_ERR_SHAPE, "%s: row stride %lld < K = %lld", name, (long long)ldx, (long long)K);
+    if (!aligned16(x) || ldx % 8 != 0)
+        return fail(NVFP4_ERR_ALIGN, "%s: base must be 16-byte aligned and the row stride a multiple of 8 elements", name);
+    return NVFP4_OK;
+}
+
+// An NVFP4 tensor [rows, K]: codes [rows, K/2] (stride ldc bytes) + scales [rows, K/16] (stride lds).
+nvfp4_status check_nvfp4(const uint8_t* codes, int64_t ldc, const uint8_t* scales, int64_t lds, int64_t rows,
+                         int64_t K, const char* name) {
+    if (rows == 0 || K == 0) return NVFP4_OK;
+    if (!codes || !scales) return fail(NVFP4_ERR_NULL, "%s codes or scales is NULL", name);
+    if (ldc < K / 2 || lds < K / 16)
+        return fail(NVFP4_ERR_SHAPE, "%s: strides (%lld, %lld) smaller than a row (%lld, %lld)", name,
+                    (long long)ldc, (long long)lds, (long long)(K / 2), (long long)(K / 16));
+    if (!aligned16(codes) || !aligned16(scales) || ldc % 16 != 0 || lds % 16 != 0)
+        return fail(NVFP4_ERR_ALIGN, "%s: codes/scales must be 16-byte aligned with strides a multiple of 16 bytes", name);
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_NULL: return "null pointer";
+        case NVFP4_ERR_SHAPE: return "invalid shape or stride";
+        case NVFP4_ERR_ALIGN: return "misaligned pointer or stride";
+        case NVFP4_ERR_SEGMENTS: return "invalid segment table";
+        case NVFP4_ERR_SCALE: return "global scale not finite and positive";
+        case NVFP4_ERR_EPILOGUE: return "invalid epilogue or output type";
+        case NVFP4_ERR_WORKSPACE: return "workspace too small";
+        case NVFP4_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
+nvfp4_status nvfp4_global_scale(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx, float* g_out,
+                                void* stream) {
+    nvfp4_status st = check_bf16_matrix(x_bf16, rows, K, ldx, "x");
+    if (st != NVFP4_OK) return st;
+    if (!g_out) return fail(NVFP4_ERR_NULL, "g_out is NULL");
+    if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(NVFP4_ERR_ALIGN, "g_out must be 4-byte aligned");
+    return hip_status(nvfp4::launch_global_scale(static_cast<const uint16_t*>(x_bf16), rows, K, ldx, g_out,
+                                                 static_cast<hipStream_t>(stream)),
+                      "nvfp4_global_scale launch");
+}
+
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx, float g, uint8_t* codes,
+                            int64_t ldc, uint8_t* scales, int64_t lds, void* stream) {
+    if (rows < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+    nvfp4_status st = check_bf16_matrix(x_bf16, rows, K, ldx, "x");
+    if (st != NVFP4_OK) return st;
+    st = check_nvfp4(codes, ldc, scales, lds, rows, K, "output");
+    if (st != NVFP4_OK) return st;
+    if (!good_scale(g)) return fail(NVFP4_ERR_SCALE, "global scale g = %g must be finite and > 0", (double)g);
+    if (rows == 0 || K == 0) return ok();
+    if ((uint64_t)rows * (uint64_t)((K / 16 + 63) / 64) > (uint64_t)0x1FFFFFFFCull)
+        return fail(NVFP4_ERR_SHAPE, "tensor too large for one launch");
+    return hip_status(nvfp4::launch_quantize(static_cast<const uint16_t*>(x_bf16), rows, K, ldx, g, codes, ldc,
+                                             scales, lds, static_cast<hipStream_t>(stream)),
+                      "nvfp4_quantize launch");
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s, float g_a,
+                        const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, int64_t M,
+                        int64_t N, int64_t K, const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+    if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return fail(NVFP4_ERR_SHAPE, "M or N too large");
+    nvfp4_status st = check_nvfp4(a_codes, lda_c, a_scales, lda_s, M, K, "A");
+    if (st != NVFP4_OK) return st;
+    st = check_nvfp4(w_codes, ldw_c, w_scales, ldw_s, N, K, "W");
+    if (st != NVFP4_OK) return st;
+    if (!segs || !g_w) return fail(NVFP4_ERR_NULL, "segment table or g_w is NULL");
+    if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
+        return fail(NVFP4_ERR_SEGMENTS, "n_segs = %d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);
+    if (!good_scale(g_a)) return fail(NVFP4_ERR_SCALE, "g_a = %g must be finite and > 0", (double)g_a);
+
+    nvfp4::SegParams sp = {};
+    sp.n_segs = n_segs;
+    int64_t expect = 0;
+    for (int s = 0; s < n_segs; ++s) {
+        const nvfp4_segment& sg = segs[s];
+        if (sg.n_begin != expect || sg.n_len <= 0)
+            return fail(NVFP4_ERR_SEGMENTS, "segment %d [%lld, +%lld) must start at %lld and be non-empty", s,
+                        (long long)sg.n_begin, (long long)sg.n_len, (long long)expect);
+        expect = sg.n_begin + sg.n_len;
+        if (!good_scale(g_w[s])) return fail(NVFP4_ERR_SCALE, "g_w[%d] = %g must be finite and > 0", s, (double)g_w[s]);
+        if (sg.epilogue < NVFP4_EPI_NONE || sg.epilogue > NVFP4_EPI_GDN_DECAY)
+            return fail(NVFP4_ERR_EPILOGUE, "segment %d: unknown epilogue %d", s, sg.epilogue);
+        if (sg.out_dtype != NVFP4_OUT_F32 && sg.out_dtype != NVFP4_OUT_BF16)
+            return fail(NVFP4_ERR_EPILOGUE, "segment %d: unknown output type %d", s, sg.out_dtype);
+        if (sg.epilogue != NVFP4_EPI_NONE && sg.out_dtype != NVFP4_OUT_F32)
+            return fail(NVFP4_ERR_EPILOGUE, "segment %d: gate epilogues write FP32", s);
+        if (sg.epilogue == NVFP4_EPI_GDN_DECAY && (!sg.A_log || !sg.dt_bias))
+            return fail(NVFP4_ERR_EPILOGUE, "segment %d: GDN decay needs A_log and dt_bias", s);
+        const int64_t esize = sg.out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+        if (M > 0) {
+            if (!sg.out) return fail(NVFP4_ERR_NULL, "segment %d: out is NULL", s);
+            if (sg.ldo < sg.n_len) return fail(NVFP4_ERR_SHAPE, "segment %d: ldo %lld < n_len %lld", s,
+                                               (long long)sg.ldo, (long long)sg.n_len);
+            if ((reinterpret_cast<uintptr_t>(sg.out) % (uintptr_t)esize) != 0)
+                return fail(NVFP4_ERR_ALIGN, "segment %d: out not aligned to its element size", s);
+        }
+        sp.n_begin[s] = sg.n_begin;
+        sp.n_end[s] = expect;
+        sp.scale[s] = g_a * g_w[s];  // RN32(g_a * g_w[s])
+        sp.epilogue[s] = sg.epilogue;
+        sp.out_dtype[s] = sg.out_dtype;
+        sp.out[s] = sg.out;
+        sp.ldo[s] = sg.ldo;
+        sp.A_log[s] = sg.A_log;
+        sp.dt_bias[s] = sg.dt_bias;
+    }
+    if (expect != N) return fail(NVFP4_ERR_SEGMENTS, "segments cover [0, %lld), N = %lld", (long long)expect, (long long)N);
+    const size_t need = nvfp4_gemm_workspace_bytes(M, N, K);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (M == 0 || N == 0) return ok();
+    return hip_status(nvfp4::launch_gemm(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K,
+                                         sp, static_cast<hipStream_t>(stream)),
+                      "nvfp4_gemm launch");
+}
+
+}  // extern "C"

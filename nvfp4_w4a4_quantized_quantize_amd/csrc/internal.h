@@ -1,0 +1,37 @@
+// Internal declarations shared by the HIP sources of libnvfp4.so (not installed, not part of the
+// C interface in include/nvfp4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+// Segment table as passed to the GEMM kernel by value (kernel-argument memory).
+struct SegParams {
+    int32_t n_segs;
+    int32_t pad_;
+    int64_t n_begin[NVFP4_MAX_SEGMENTS];
+    int64_t n_end[NVFP4_MAX_SEGMENTS];     // exclusive
+    float scale[NVFP4_MAX_SEGMENTS];       // RN32(g_a * g_w[s])
+    int32_t epilogue[NVFP4_MAX_SEGMENTS];
+    int32_t out_dtype[NVFP4_MAX_SEGMENTS];
+    void* out[NVFP4_MAX_SEGMENTS];
+    int64_t ldo[NVFP4_MAX_SEGMENTS];
+    const float* A_log[NVFP4_MAX_SEGMENTS];
+    const float* dt_bias[NVFP4_MAX_SEGMENTS];
+};
+
+// Launchers: shapes are validated by the C interface before these are called.
+hipError_t launch_global_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float* g_out,
+                               hipStream_t stream);
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float g,
+                           uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                           hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                       const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                       int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gdn_decay_array.argtypes = [P, i64, i64, P, P, P]
         L.oracle_e4m3_from_float_array.restype = None
         L.oracle_e4m3_from_float_array.argtypes = [P, i64, P]
+        L.oracle_num_threads.restype = i32
+        L.oracle_num_threads.argtypes = []
         L.oracle_e2m1_from_float_array.restype = None
         L.oracle_e2m1_from_float_array.argtypes = [P, i64, P]
         _lib = L
@@ -83,6 +85,11 @@ def lib() -> ctypes.CDLL:
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP row loops use."""
+    return int(lib().oracle_num_threads())
 
 
 # ---------------------------------------------------------------- format helpers

@@ -29,6 +29,9 @@
  *  - GEMM products are accumulated exactly (integers in units of 2^-20), then scaled in double.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -140,6 +143,7 @@ int oracle_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, flo
     e4m3_grid(g4);
     e2m1_grid(g2);
     float t = 6.0f * g;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < K / 16; ++b) {
             float xs[16];
@@ -203,6 +207,7 @@ int oracle_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, int64_t ld
     if (K % 16 != 0) return -1;
     int32_t* wq = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N * K));
     if (!wq) return -2;
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
             wq[n * K + k] = (int32_t)deq_units(w_codes, w_scales, n, k, ldw_c, ldw_s);
@@ -274,4 +279,13 @@ void oracle_e2m1_from_float_array(const float* v, int64_t n, uint8_t* out) {
     double grid[8];
     e2m1_grid(grid);
     for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)nearest_even((double)v[i], grid, 8);
+}
+
+/* Number of threads the OpenMP row loops use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

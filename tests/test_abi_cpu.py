@@ -1,0 +1,118 @@
+"""The C interface without a GPU: the library loads, exports every function include/nvfp4.h declares,
+and rejects invalid arguments with the documented status before anything is launched. Pointers here
+are fake aligned addresses; no call in this file reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_w4a4_quantized_quantize_amd as nv
+from nvfp4_w4a4_quantized_quantize_amd import build as hipbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        hipbuild.build()
+    return nv.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(nv.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert nv.status_string(s) not in ("", "unknown status")
+    assert nv.status_string(99) == "unknown status"
+    assert nv.lib().nvfp4_gemm_workspace_bytes(32768, 12352, 5120) == 0
+
+
+A16 = 0x100000  # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def q(L, x=A16, rows=4, K=64, ldx=64, g=1.0, codes=A16, ldc=32, scales=A16, lds=16):
+    return L.nvfp4_quantize(x, rows, K, ldx, g, codes, ldc, scales, lds, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scales=None), 1),
+    (dict(K=24, ldx=32), 2), (dict(rows=-1), 2), (dict(ldx=56), 2), (dict(ldc=16), 2), (dict(lds=0), 2),
+    (dict(x=A16 + 8), 3), (dict(ldx=68), 3), (dict(codes=A16 + 4), 3), (dict(ldc=40), 3), (dict(lds=24), 3),
+    (dict(g=0.0), 5), (dict(g=-1.0), 5), (dict(g=float("inf")), 5), (dict(g=float("nan")), 5),
+])
+def test_quantize_rejects(L, kw, status):
+    assert q(L, **kw) == status
+    assert nv.last_error() != ""
+
+
+def test_quantize_empty_is_ok_without_launch(L):
+    assert q(L, rows=0) == 0
+    assert q(L, K=0, ldx=0) == 0
+
+
+def test_global_scale_rejects(L):
+    assert L.nvfp4_global_scale(None, 4, 64, 64, A16, None) == 1
+    assert L.nvfp4_global_scale(A16, 4, 64, 64, None, None) == 1
+    assert L.nvfp4_global_scale(A16 + 2, 4, 64, 64, A16, None) == 3
+    assert L.nvfp4_global_scale(A16, 4, 64, 60, A16, None) == 2
+    assert L.nvfp4_global_scale(A16, 4, 64, 64, A16 + 2, None) == 3
+
+
+def seg_array(specs):
+    arr = (nv._Segment * max(1, len(specs)))()
+    for i, s in enumerate(specs):
+        arr[i] = nv._Segment(*s)
+    return arr
+
+
+def g(L, M=8, N=64, K=64, segs=None, g_w=None, n_segs=None, g_a=1.0, a_codes=A16, lda_c=32, a_scales=A16,
+      lda_s=16, w_codes=A16, ldw_c=32, w_scales=A16, ldw_s=16, ws=None, ws_bytes=0):
+    if segs is None:
+        segs = [(0, N, 0, 0, A16, N, None, None)]
+    n = len(segs) if n_segs is None else n_segs
+    if g_w is None:
+        g_w = [1.0] * max(1, len(segs))
+    gw = (ctypes.c_float * max(1, len(g_w)))(*g_w)
+    return L.nvfp4_gemm(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, M, N, K,
+                        seg_array(segs), gw, n, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_codes=None), 1), (dict(w_scales=None), 1),
+    (dict(K=40), 2), (dict(M=-1), 2), (dict(lda_c=16), 2), (dict(ldw_s=0), 2),
+    (dict(a_codes=A16 + 1), 3), (dict(lda_c=40), 3), (dict(ldw_s=24), 3),
+    (dict(n_segs=0), 4), (dict(n_segs=17), 4),
+    (dict(segs=[(0, 32, 0, 0, A16, 32, None, None)]), 4),
+    (dict(segs=[(0, 32, 0, 0, A16, 64, None, None), (16, 48, 0, 0, A16, 64, None, None)]), 4),
+    (dict(segs=[(0, 32, 0, 0, A16, 64, None, None), (40, 24, 0, 0, A16, 64, None, None)]), 4),
+    (dict(segs=[(0, 0, 0, 0, A16, 64, None, None), (0, 64, 0, 0, A16, 64, None, None)]), 4),
+    (dict(g_a=0.0), 5), (dict(g_w=[float("nan")]), 5), (dict(g_w=[-2.0]), 5),
+    (dict(segs=[(0, 64, 3, 0, A16, 64, None, None)]), 6),
+    (dict(segs=[(0, 64, 0, 2, A16, 64, None, None)]), 6),
+    (dict(segs=[(0, 64, 1, 1, A16, 64, None, None)]), 6),
+    (dict(segs=[(0, 64, 2, 0, A16, 64, None, A16)]), 6),
+    (dict(segs=[(0, 64, 0, 0, None, 64, None, None)]), 1),
+    (dict(segs=[(0, 64, 0, 0, A16, 32, None, None)]), 2),
+    (dict(segs=[(0, 64, 0, 0, A16 + 2, 64, None, None)]), 3),
+])
+def test_gemm_rejects(L, kw, status):
+    assert g(L, **kw) == status, nv.last_error()
+    assert nv.last_error() != ""
+
+
+def test_gemm_empty_shapes_ok_without_launch(L):
+    assert g(L, M=0) == 0
+    assert g(L, N=0, segs=[(0, 0, 0, 0, A16, 0, None, None)], n_segs=0) == 4  # still needs one segment
