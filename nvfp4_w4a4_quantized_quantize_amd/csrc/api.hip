@@ -163,6 +163,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
         sp.ldo[s] = sg.ldo;
         sp.A_log[s] = sg.A_log;
         sp.dt_bias[s] = sg.dt_bias;
+        const int64_t per16 = 16 / esize;  // elements per 16 bytes
+        if (sg.epilogue == NVFP4_EPI_NONE && aligned16(sg.out) && sg.ldo % per16 == 0 && sg.n_begin % per16 == 0)
+            sp.vec_mask |= 1u << s;
     }
     if (expect != N) return fail(NVFP4_ERR_SEGMENTS, "segments cover [0, %lld), N = %lld", (long long)expect, (long long)N);
     const size_t need = nvfp4_gemm_workspace_bytes(M, N, K);

@@ -12,7 +12,7 @@ namespace nvfp4 {
 // Segment table as passed to the GEMM kernel by value (kernel-argument memory).
 struct SegParams {
     int32_t n_segs;
-    int32_t pad_;
+    uint32_t vec_mask;                     // bit s: segment s may use 16-byte epilogue stores
     int64_t n_begin[NVFP4_MAX_SEGMENTS];
     int64_t n_end[NVFP4_MAX_SEGMENTS];     // exclusive
     float scale[NVFP4_MAX_SEGMENTS];       // RN32(g_a * g_w[s])
