@@ -35,6 +35,22 @@ PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0  # read bf16, write codes + scales
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded from rocprofv3 counters for this kernel source, else None."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)[kernel]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            same = hashlib.sha256(f.read()).hexdigest() == rec["sha256"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if not same or rec["workload"] != workload:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"], {"read_bytes": rec["read_bytes"], "write_bytes": rec["write_bytes"],
+                                                    "from": rec["summary"]}
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -89,7 +105,11 @@ class Step:
         nv.gemm(self.a_codes, self.a_scales, self.g_a, self.w_codes, self.w_scales, self.segments)
 
 
-def run_gpu(step: Step, steps: int, warmup: int) -> dict:
+def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
+    """Time `steps` steps with HIP events on the library's stream. With flush_mb > 0 a buffer of that
+    size is overwritten before every step (outside the timed kernels) so that a working set smaller
+    than the 256 MB last-level cache is read from HBM, and the step time is the sum of the kernels."""
+    flush = torch.empty(flush_mb * (1 << 20) // 4, dtype=torch.float32, device="cuda") if flush_mb else None
     for _ in range(warmup):
         step.quantize()
         step.gemm()
@@ -99,6 +119,8 @@ def run_gpu(step: Step, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush.zero_()
         ev[i][0].record(stream)
         step.quantize()
         ev[i][1].record(stream)
@@ -108,8 +130,20 @@ def run_gpu(step: Step, steps: int, warmup: int) -> dict:
     wall = time.perf_counter() - t0
     q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
     g_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
-    total_ms = ev[0][0].elapsed_time(ev[-1][2])
-    return {"wall_s": wall, "step_ms": total_ms / steps, "quant_ms": float(np.mean(q_ms)),
+    # the quantizer alone, 20 back-to-back launches (its event time inside a step also holds the gap
+    # after the previous step's GEMM); the 335 MB activation does not fit the 256 MB last-level cache
+    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qa.record(stream)
+    for _ in range(20):
+        step.quantize()
+    qb.record(stream)
+    torch.cuda.synchronize()
+    quant_iso_ms = qa.elapsed_time(qb) / 20
+    if flush is None:
+        step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    else:
+        step_ms = float(np.mean(np.array(q_ms) + np.array(g_ms)))
+    return {"wall_s": wall, "step_ms": step_ms, "quant_ms": float(np.mean(q_ms)), "quant_iso_ms": quant_iso_ms,
             "gemm_ms": float(np.mean(g_ms)), "quant_ms_med": float(np.median(q_ms)),
             "gemm_ms_med": float(np.median(g_ms))}
 
@@ -180,6 +214,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-quant", type=int, default=32768)
     ap.add_argument("--cpu-rows-gemm", type=int, default=4096)
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="overwrite a buffer of this size before each step (-1: 512 MB when the step's "
+                         "working set is below 1 GB, else none)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -201,14 +238,34 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     log(f"[gpu] warmup {args.warmup}, timing {args.steps} steps")
-    r = run_gpu(step, args.steps, args.warmup)
+    # a step whose working set fits the last-level cache would otherwise be served from it
+    work_mb = (case.M * case.K * 2.5625 + (case.M + case.N) * case.K * 0.5625 +
+               sum(case.M * sg.n * 4 for sg in case.segments)) / 2 ** 20
+    flush_mb = args.flush_mb if args.flush_mb >= 0 else (0 if work_mb > 1024 else 512)
+    r = run_gpu(step, args.steps, args.warmup, flush_mb)
     M, N, K = case.M, case.N, case.K
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (r["gemm_ms"] * 1e-3) / 1e12
     q_bytes = QUANT_BYTES_PER_ELEM * M * K
-    q_gbps = q_bytes / (r["quant_ms"] * 1e-3) / 1e9
-    log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {r['quant_ms']:.3f} ms ({q_gbps:.0f} GB/s), "
-        f"gemm {r['gemm_ms']:.3f} ms ({gemm_tflops:.0f} TFLOP/s)")
+    q_gbps = q_bytes / (r["quant_iso_ms"] * 1e-3) / 1e9
+    out_bytes = sum(M * s.n * (4 if s.out_dtype == wl.OUT_F32 else 2) for s in case.segments)
+    gemm_bytes = 0.5625 * (M + N) * K + out_bytes  # codes + scales of A and W, plus the outputs
+    gemm_gbps = gemm_bytes / (r["gemm_ms"] * 1e-3) / 1e9
+    # the GEMM's bound: dense FP16 MFMA above the ridge point (peak FLOP/s per HBM byte/s), HBM below
+    mfma_bound = flops / gemm_bytes >= PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {r['quant_iso_ms']:.3f} ms ({q_gbps:.0f} GB/s), "
+        f"gemm {r['gemm_ms']:.3f} ms ({gemm_tflops:.0f} TFLOP/s, {gemm_gbps:.0f} GB/s)")
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": gemm_tflops / PEAK_F16_MFMA_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gemm_gbps / PEAK_HBM_GBPS}
+    tr = measured_traffic("gemm_kernel", case.name)
+    roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
+                 "kernel": "gemm_kernel", "avg_ms": r["gemm_ms"], "algorithmic_flop": flops,
+                 "algorithmic_bytes": gemm_bytes})
+    trq = measured_traffic("quantize_kernel", f"x_{M}x{K}")
     out = {
         "metric": "NVFP4 W4A4 GEMM TFLOPS at 32K-token prefill + quantize GB/s, % of roofline",
         "value": flops / (r["step_ms"] * 1e-3) / 1e12,
@@ -220,19 +277,21 @@ def main() -> int:
         "data": "synthetic (seeded; heavy-tailed activations with outlier channels, per-segment weight spreads)",
         "config": {"workload": case.name, "M": M, "N": N, "K": K,
                    "segments": ",".join(f"{s.name}{s.n}" for s in case.segments),
-                   "epilogues": "q,k,v,z bf16; b sigmoid f32; a gdn_decay f32"},
+                   "epilogues": ";".join(f"{s.name}:{['none', 'sigmoid', 'gdn_decay'][s.epilogue]}/"
+                                         f"{['f32', 'bf16'][s.out_dtype]}" for s in case.segments)},
         "gemm_tflops": gemm_tflops,
+        "gemm_gbps": gemm_gbps,
         "quantize_gbps": q_gbps,
-        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / PEAK_F16_MFMA_TFLOPS, "traffic": None,
-                     "kernel": "gemm_kernel", "avg_ms": r["gemm_ms"], "algorithmic_flop": flops},
+        "roofline": roof,
         "roofline_quantize": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                              "frac": q_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "quantize_kernel",
-                              "avg_ms": r["quant_ms"], "algorithmic_bytes": q_bytes},
+                              "frac": q_gbps / PEAK_HBM_GBPS, "traffic": trq[0] if trq else None,
+                              "traffic_detail": trq[1] if trq else None, "kernel": "quantize_kernel",
+                              "avg_ms": r["quant_iso_ms"], "avg_ms_in_step": r["quant_ms"],
+                              "algorithmic_bytes": q_bytes},
     }
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on a sample")
-        out["cpu_baseline"] = run_cpu_baseline(step, args.cpu_rows_quant, args.cpu_rows_gemm)
+        out["cpu_baseline"] = run_cpu_baseline(step, min(args.cpu_rows_quant, M), min(args.cpu_rows_gemm, M))
     print(json.dumps(out), flush=True)
     return 0
 
