@@ -172,8 +172,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (M == 0 || N == 0) return ok();
-    return hip_status(nvfp4::launch_gemm(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K,
-                                         sp, static_cast<hipStream_t>(stream)),
+    const auto launch = M <= nvfp4::SKINNY_MAX_M ? nvfp4::launch_gemm_skinny : nvfp4::launch_gemm_tiled;
+    return hip_status(launch(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
+                             static_cast<hipStream_t>(stream)),
                       "nvfp4_gemm launch");
 }
 

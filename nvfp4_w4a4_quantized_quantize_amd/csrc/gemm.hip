@@ -30,18 +30,10 @@
 //  * Epilogue: accumulators are staged per wave through LDS; whole 32-column groups of a plain
 //    segment are scaled and written with 16-byte stores, other columns (gates, segment boundaries,
 //    the N tail) element by element.
-#include "internal.h"
+#include "device_common.h"
 
 namespace nvfp4 {
 namespace {
-
-typedef _Float16 half_t;
-typedef half_t half2_t __attribute__((ext_vector_type(2)));
-typedef half_t half8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 256;
 constexpr int NTHREADS = 256;
@@ -103,16 +95,6 @@ struct Loader {
     }
 };
 
-// 8 codes (one dword) times one FP16 block scale -> 8 exact FP16 values.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, half_t s) {
-    const half2_t ss = {s, s};
-    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
 // The two E4M3 scale bytes of (sub-chunk c, lane half lh) as FP16.
 __device__ __forceinline__ half2_t scale_pair(const u32x4& s, int c, int lh) {
     const uint32_t word = s[c] >> (lh << 4);  // bytes 4c + 2lh, 4c + 2lh + 1
@@ -151,23 +133,6 @@ __device__ __forceinline__ void read_scales(u32x4 (&as)[4], u32x4 (&bs)[4], cons
             }
         }
     }
-}
-
-__device__ __forceinline__ float sigmoid_f32(float y) { return 1.0f / (1.0f + expf(-y)); }
-
-__device__ __forceinline__ float softplus_f32(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
-
-__device__ __forceinline__ int segment_of(const SegParams& sp, int64_t col) {
-    int s = 0;
-    for (int t = 1; t < sp.n_segs; ++t)
-        if (col >= sp.n_begin[t]) s = t;
-    return s;
-}
-
-__device__ __forceinline__ float apply_gate(float y, int epi, float a_coef, float dtb) {
-    if (epi == NVFP4_EPI_SIGMOID) return sigmoid_f32(y);
-    if (epi == NVFP4_EPI_GDN_DECAY) return expf(-(a_coef * softplus_f32(y + dtb)));
-    return y;
 }
 
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
@@ -398,9 +363,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
-                       const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
-                       int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream) {
+hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                             const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                             int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(tiles_m * tiles_n)), dim3(NTHREADS), 0, stream, a_codes,

@@ -30,8 +30,16 @@ hipError_t launch_global_scale(const uint16_t* x, int64_t rows, int64_t K, int64
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float g,
                            uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
                            hipStream_t stream);
-hipError_t launch_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
-                       const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
-                       int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+
+// Activation row counts up to SKINNY_MAX_M run on the skinny (decode) kernel, larger ones on the
+// tiled kernel.
+constexpr int64_t SKINNY_MAX_M = 64;
+
+hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                             const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                             int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                              const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
 
 }  // namespace nvfp4
