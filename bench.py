@@ -62,7 +62,7 @@ def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
 class Step:
     """Device buffers and the launches of one step of the fused GDN input projection."""
 
-    def __init__(self, case: wl.GemmCase, seed: int = 0):
+    def __init__(self, case: wl.GemmCase, seed: int = 0, copies: int = 1):
         self.case = case
         M, K, N = case.M, case.K, case.N
         dev = torch.device("cuda")
@@ -82,6 +82,12 @@ class Step:
             nv.quantize(wt, g, self.w_codes[n0:n0 + seg.n], self.w_scales[n0:n0 + seg.n])
             self.g_w.append(g)
             n0 += seg.n
+        # extra copies of the quantized weights, used in turn by consecutive steps (as consecutive
+        # layers would), so that a small working set is still read from HBM
+        self.w_copies = [(self.w_codes, self.w_scales)]
+        for _ in range(copies - 1):
+            self.w_copies.append((self.w_codes.clone(), self.w_scales.clone()))
+        self.calls = 0
         # static activation calibration
         self.g_a = float(nv.global_scale(self.x).item())
         self.a_codes, self.a_scales = nv.alloc_nvfp4(M, K, dev)
@@ -102,7 +108,9 @@ class Step:
         nv.quantize(self.x, self.g_a, self.a_codes, self.a_scales)
 
     def gemm(self):
-        nv.gemm(self.a_codes, self.a_scales, self.g_a, self.w_codes, self.w_scales, self.segments)
+        wc, ws = self.w_copies[self.calls % len(self.w_copies)]
+        self.calls += 1
+        nv.gemm(self.a_codes, self.a_scales, self.g_a, wc, ws, self.segments)
 
 
 def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
@@ -139,11 +147,21 @@ def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
     qb.record(stream)
     torch.cuda.synchronize()
     quant_iso_ms = qa.elapsed_time(qb) / 20
+    # the GEMM alone, back to back over the weight copies (only meaningful when there are several:
+    # a single copy would be served from the last-level cache)
+    n_iso = max(steps, 4 * len(step.w_copies))
+    qa.record(stream)
+    for _ in range(n_iso):
+        step.gemm()
+    qb.record(stream)
+    torch.cuda.synchronize()
+    gemm_iso_ms = qa.elapsed_time(qb) / n_iso
     if flush is None:
         step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
     else:
         step_ms = float(np.mean(np.array(q_ms) + np.array(g_ms)))
     return {"wall_s": wall, "step_ms": step_ms, "quant_ms": float(np.mean(q_ms)), "quant_iso_ms": quant_iso_ms,
+            "gemm_iso_ms": gemm_iso_ms,
             "gemm_ms": float(np.mean(g_ms)), "quant_ms_med": float(np.median(q_ms)),
             "gemm_ms_med": float(np.median(g_ms))}
 
@@ -215,8 +233,7 @@ def main() -> int:
     ap.add_argument("--cpu-rows-quant", type=int, default=32768)
     ap.add_argument("--cpu-rows-gemm", type=int, default=4096)
     ap.add_argument("--flush-mb", type=int, default=-1,
-                    help="overwrite a buffer of this size before each step (-1: 512 MB when the step's "
-                         "working set is below 1 GB, else none)")
+                    help="overwrite a buffer of this size before each step (-1: none)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -229,7 +246,13 @@ def main() -> int:
         return 2
     nv.lib()  # fail loudly if the HIP library is missing
     case = wl.ALL[args.workload]
-    step = Step(case)
+    # a step whose working set fits the 256 MB last-level cache would be served from it: such steps
+    # rotate through copies of the weights, 1 GiB in all
+    work_mb = (case.M * case.K * 2.5625 + (case.M + case.N) * case.K * 0.5625 +
+               sum(case.M * sg.n * 4 for sg in case.segments)) / 2 ** 20
+    w_mb = case.N * case.K * 0.5625 / 2 ** 20
+    copies = 1 if work_mb > 1024 else int(min(64, max(2, np.ceil(1024 / w_mb))))
+    step = Step(case, copies=copies)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -238,32 +261,33 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     log(f"[gpu] warmup {args.warmup}, timing {args.steps} steps")
-    # a step whose working set fits the last-level cache would otherwise be served from it
-    work_mb = (case.M * case.K * 2.5625 + (case.M + case.N) * case.K * 0.5625 +
-               sum(case.M * sg.n * 4 for sg in case.segments)) / 2 ** 20
-    flush_mb = args.flush_mb if args.flush_mb >= 0 else (0 if work_mb > 1024 else 512)
+    flush_mb = max(args.flush_mb, 0)
     r = run_gpu(step, args.steps, args.warmup, flush_mb)
+    # the GEMM's average launch duration: inside the step when the weights are not rotated, else
+    # back to back over the copies (a few microseconds of event overhead per step would count)
+    gemm_ms = r["gemm_ms"] if copies == 1 else r["gemm_iso_ms"]
     M, N, K = case.M, case.N, case.K
     flops = 2.0 * M * N * K
-    gemm_tflops = flops / (r["gemm_ms"] * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     q_bytes = QUANT_BYTES_PER_ELEM * M * K
     q_gbps = q_bytes / (r["quant_iso_ms"] * 1e-3) / 1e9
     out_bytes = sum(M * s.n * (4 if s.out_dtype == wl.OUT_F32 else 2) for s in case.segments)
     gemm_bytes = 0.5625 * (M + N) * K + out_bytes  # codes + scales of A and W, plus the outputs
-    gemm_gbps = gemm_bytes / (r["gemm_ms"] * 1e-3) / 1e9
+    gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     # the GEMM's bound: dense FP16 MFMA above the ridge point (peak FLOP/s per HBM byte/s), HBM below
     mfma_bound = flops / gemm_bytes >= PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {r['quant_iso_ms']:.3f} ms ({q_gbps:.0f} GB/s), "
-        f"gemm {r['gemm_ms']:.3f} ms ({gemm_tflops:.0f} TFLOP/s, {gemm_gbps:.0f} GB/s)")
+        f"gemm {gemm_ms:.4f} ms ({gemm_tflops:.0f} TFLOP/s, {gemm_gbps:.0f} GB/s), weight copies {copies}")
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": gemm_tflops / PEAK_F16_MFMA_TFLOPS}
     else:
         roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gemm_gbps / PEAK_HBM_GBPS}
-    tr = measured_traffic("gemm_kernel", case.name)
+    kernel = "gemm_skinny_kernel" if M <= 64 else "gemm_kernel"
+    tr = measured_traffic(kernel, case.name)
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
-                 "kernel": "gemm_kernel", "avg_ms": r["gemm_ms"], "algorithmic_flop": flops,
+                 "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,
                  "algorithmic_bytes": gemm_bytes})
     trq = measured_traffic("quantize_kernel", f"x_{M}x{K}")
     out = {

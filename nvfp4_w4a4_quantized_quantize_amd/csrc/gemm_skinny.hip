@@ -22,7 +22,7 @@
 //    columns of B; at step j (0..7) each lane feeds its elements [8j, 8j + 8). Both operands are
 //    dequantized to FP16 exactly (see dequant8), products are exact in FP32 and accumulate in FP32.
 //    MT = ceil(M / 16) activation tiles and NT weight tiles per wave.
-//  * The next chunk's loads are issued before the current chunk is dequantized and multiplied.
+//  * The loads of the next DEPTH chunks are in flight while a chunk is dequantized and multiplied.
 //  * The KW partial sums meet in LDS and are added in wave order (deterministic), then scaled by
 //    g_a * g_w of the column's segment, gated and stored, consecutive threads on consecutive columns.
 #include <algorithm>
@@ -32,8 +32,9 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int MAX_WAVES = 8;
+constexpr int MAX_WAVES = 4;  // K-split of a workgroup
 constexpr int CHUNK = 256;  // K elements per chunk: 128 code bytes and 16 scale bytes per row
+constexpr int DEPTH = 2;    // chunks in flight ahead of the one being multiplied
 
 // One lane's share of one row of a chunk: 64 codes (two 16-byte pieces) and their 4 scale bytes.
 struct RowFrag {
@@ -83,20 +84,13 @@ struct Frags {
 };
 
 template <int MT, int NT>
-__device__ __forceinline__ void load_chunk(Frags<MT, NT>& f, const uint8_t* const (&wc)[NT],
-                                           const uint8_t* const (&ws)[NT], const uint8_t* const (&ac)[MT],
-                                           const uint8_t* const (&as)[MT], int64_t c, bool tail, int g, int64_t K) {
-    if (!tail) {
+__device__ __forceinline__ void load_full_chunk(Frags<MT, NT>& f, const uint8_t* const (&wc)[NT],
+                                                const uint8_t* const (&ws)[NT], const uint8_t* const (&ac)[MT],
+                                                const uint8_t* const (&as)[MT], int64_t c) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) load_full(wc[t], ws[t], c, f.w[t]);
+    for (int t = 0; t < NT; ++t) load_full(wc[t], ws[t], c, f.w[t]);
 #pragma unroll
-        for (int u = 0; u < MT; ++u) load_full(ac[u], as[u], c, f.a[u]);
-    } else {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) load_tail(wc[t], ws[t], c, g, K, f.w[t]);
-#pragma unroll
-        for (int u = 0; u < MT; ++u) load_tail(ac[u], as[u], c, g, K, f.a[u]);
-    }
+    for (int u = 0; u < MT; ++u) load_full(ac[u], as[u], c, f.a[u]);
 }
 
 template <int MT, int NT>
@@ -165,15 +159,41 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (c_lo < c_hi) {
-        Frags<MT, NT> cur;
-        load_chunk<MT, NT>(cur, wc, ws, ac, as, c_lo, c_lo >= nfull, g, K);
-        for (int64_t c = c_lo; c < c_hi; ++c) {
-            Frags<MT, NT> nxt;
-            if (c + 1 < c_hi) load_chunk<MT, NT>(nxt, wc, ws, ac, as, c + 1, c + 1 >= nfull, g, K);
-            compute_chunk<MT, NT>(cur, acc);
-            cur = nxt;
+    // Full chunks [c_lo, c_end) go through a ring of DEPTH + 1 register buffers: chunk c is multiplied
+    // while chunks c + 1 .. c + DEPTH are in flight. The loop is unrolled over the ring, so no buffer
+    // is ever copied, and its loads are unconditional (indices past the range are clamped to its last
+    // chunk), so the compiler can wait for exactly one chunk's loads at a time; a copy or a load under
+    // a branch would make it wait for all of them.
+    const int64_t c_end = std::min(c_hi, nfull);
+    if (c_lo < c_end) {
+        constexpr int RING = DEPTH + 1;
+        Frags<MT, NT> f[RING];
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) load_full_chunk<MT, NT>(f[i], wc, ws, ac, as, std::min(c_lo + i, c_end - 1));
+        int64_t c = c_lo;
+        for (; c + RING <= c_end; c += RING) {
+#pragma unroll
+            for (int i = 0; i < RING; ++i) {
+                load_full_chunk<MT, NT>(f[(i + DEPTH) % RING], wc, ws, ac, as, std::min(c + i + DEPTH, c_end - 1));
+                // keep the loads ahead of this chunk's arithmetic: sunk below it they would be waited for
+                __builtin_amdgcn_sched_barrier(0);
+                compute_chunk<MT, NT>(f[i], acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        // fewer than RING chunks left, already loaded into f[0 ..]
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i)
+            if (c + i < c_end) compute_chunk<MT, NT>(f[i], acc);
+    }
+    // the chunk that crosses K, if any, is the last chunk of the last wave
+    if (c_hi > nfull && c_lo <= nfull) {
+        Frags<MT, NT> t;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) load_tail(wc[i], ws[i], nfull, g, K, t.w[i]);
+#pragma unroll
+        for (int u = 0; u < MT; ++u) load_tail(ac[u], as[u], nfull, g, K, t.a[u]);
+        compute_chunk<MT, NT>(t, acc);
     }
 
     constexpr int TILE = NT * MT * 256;
@@ -213,12 +233,14 @@ skinny_fn pick_nt(int nt) {
     return gemm_skinny_kernel<MT, 1>;
 }
 
-}  // namespace
-
+// Waves per workgroup splitting K: depends on K alone, so the order of the additions (and so every
+// output bit) is the same for any N, column tile or segment table.
 int skinny_waves(int64_t K) {
     const int64_t nch = (K + CHUNK - 1) / CHUNK;
-    return (int)std::min<int64_t>(MAX_WAVES, std::max<int64_t>(1, nch / 4));
+    return (int)std::min<int64_t>(4, std::max<int64_t>(1, nch / 4));
 }
+
+}  // namespace
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
@@ -230,7 +252,10 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8
     int nt = 1;
     while (nt < 4 && (N + 32 * nt - 1) / (32 * nt) >= 512) nt *= 2;
     if (mt >= 3) nt = std::min(nt, 2);
-    skinny_fn fn = mt == 1 ? pick_nt<1>(nt) : mt == 2 ? pick_nt<2>(nt) : mt == 3 ? pick_nt<3>(nt) : pick_nt<4>(nt);
+    const skinny_fn fn = mt == 1   ? pick_nt<1>(nt)
+                         : mt == 2 ? pick_nt<2>(nt)
+                         : mt == 3 ? pick_nt<3>(nt)
+                                   : pick_nt<4>(nt);
     const int kw = skinny_waves(K);
     const size_t lds = (size_t)kw * nt * mt * 256 * sizeof(float);
     const int64_t blocks = (N + 16 * nt - 1) / (16 * nt);

@@ -2,7 +2,7 @@
 
 Activation row counts up to 64 run on the skinny kernel: these tests cover every activation-tile
 count (M = 1 .. 64, ragged), every weight-tile width the launcher picks (N large enough for 2 and 4
-tiles of 16 rows per wave), K-splits over 1 .. 8 waves with ragged chunk counts and a ragged final
+tiles of 16 rows per wave), K-splits over 1 .. 4 waves with ragged chunk counts and a ragged final
 chunk, padded input strides, multi-segment tables with gate epilogues, bitwise agreement of a fused
 call with the same modules called one by one, repeatability, and the switch to the tiled kernel at
 M = 65. Acceptance is the bound stated in gpu_common.
@@ -65,7 +65,7 @@ def test_skinny_wide_weight_tiles(M):
 
 @pytest.mark.parametrize("K", [2048 + 16, 8192 + 128, 17408, 17408 + 16 * 7])
 def test_skinny_long_k_splits(K):
-    """Long K: up to 8 waves per column tile, uneven chunk counts, a partial last chunk."""
+    """Long K: up to 4 waves per column tile, uneven chunk counts, a partial last chunk."""
     rng = np.random.default_rng(K)
     M, N = 9, 70
     a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
