@@ -79,6 +79,20 @@ def lib() -> ctypes.CDLL:
         L.oracle_num_threads.argtypes = []
         L.oracle_e2m1_from_float_array.restype = None
         L.oracle_e2m1_from_float_array.argtypes = [P, i64, P]
+        L.oracle_kv_scale.restype = f32
+        L.oracle_kv_scale.argtypes = [f32]
+        L.oracle_kv_quantize.restype = None
+        L.oracle_kv_quantize.argtypes = [P, i64, i64, i64, f32, P, i64]
+        L.oracle_kv_dequantize.restype = None
+        L.oracle_kv_dequantize.argtypes = [P, i64, i64, i64, f32, P, i64]
+        L.oracle_fold_common_scale.restype = f32
+        L.oracle_fold_common_scale.argtypes = [P, i32]
+        L.oracle_fold_ratio.restype = f32
+        L.oracle_fold_ratio.argtypes = [f32, f32]
+        L.oracle_fold_scales.restype = None
+        L.oracle_fold_scales.argtypes = [P, i64, i64, i64, f32]
+        L.oracle_rmsnorm.restype = None
+        L.oracle_rmsnorm.argtypes = [P, i64, i64, i64, P, f32, P, i64, P]
         _lib = L
     return _lib
 
@@ -207,3 +221,61 @@ def gdn_decay_scalar(y: float, a_log: float, dt_bias: float) -> float:
 
 def sigmoid_scalar(y: float) -> float:
     return lib().oracle_sigmoid(float(y))
+
+
+# ---------------------------------------------------------------- serving-path companions
+def kv_scale(x_bf16: np.ndarray) -> np.float32:
+    """Static FP8 KV scale of a calibration tensor: RN32(amax / 448)."""
+    return np.float32(lib().oracle_kv_scale(tensor_amax(x_bf16)))
+
+
+def kv_quantize(x_bf16: np.ndarray, s) -> np.ndarray:
+    """bf16 bits [rows, cols] -> E4M3 bytes, q = E4M3_RNE_SAT(RN32(x / s))."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    lib().oracle_kv_quantize(_ptr(x), rows, cols, cols, float(np.float32(s)), _ptr(q), cols)
+    return q
+
+
+def kv_dequantize(q: np.ndarray, s) -> np.ndarray:
+    """E4M3 bytes -> bf16 bits, y = bf16_RNE(RN32(e4m3(q) * s))."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows, cols = q.shape
+    y = np.empty((rows, cols), np.uint16)
+    lib().oracle_kv_dequantize(_ptr(q), rows, cols, cols, float(np.float32(s)), _ptr(y), cols)
+    return y
+
+
+def fold_common_scale(g) -> np.float32:
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    return np.float32(lib().oracle_fold_common_scale(_ptr(g), len(g)))
+
+
+def fold_ratio(g, G) -> np.float32:
+    return np.float32(lib().oracle_fold_ratio(float(np.float32(g)), float(np.float32(G))))
+
+
+def fold_scales(scales: np.ndarray, ratio) -> np.ndarray:
+    """Returns a copy of the [rows, nblocks] scale bytes with the ratio folded in."""
+    out = np.array(scales, dtype=np.uint8, copy=True, order="C")
+    rows, nb = out.shape
+    lib().oracle_fold_scales(_ptr(out), rows, nb, nb, float(np.float32(ratio)))
+    return out
+
+
+def fold_group(scales_per_module, g_per_module):
+    """The fold-in repair of a fused group: (G, [folded scales per module])."""
+    G = fold_common_scale(g_per_module)
+    return G, [fold_scales(s, fold_ratio(g, G)) for s, g in zip(scales_per_module, g_per_module)]
+
+
+def rmsnorm(x_bf16: np.ndarray, w_bf16: np.ndarray, eps) -> tuple[np.ndarray, np.ndarray]:
+    """BF16 RMSNorm: (y bf16 bits [rows, K], r per row as float32)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    rows, K = x.shape
+    y = np.empty((rows, K), np.uint16)
+    r = np.empty(rows, np.float32)
+    lib().oracle_rmsnorm(_ptr(x), rows, K, K, _ptr(w), float(np.float32(eps)), _ptr(y), K, _ptr(r))
+    return y, r

@@ -18,6 +18,12 @@
  *    "Mechanism 2: the protected gate projections were the most robust".
  *  - The E2M1 and E4M3 encodings themselves follow the OCP Microscaling / FP8 definitions, which the
  *    article's reference list cites ("Microscaling Data Formats", arXiv:2310.10537).
+ *  - Companions on the same serving path (section "Serving-path companions" below): the FP8 KV cache
+ *    with calibrated static per-tensor scales -- Japanese article, "Is FP8 enough for the KV cache?
+ *    The 'ship KV scales' recipe"; the fold-in repair of the fused-module scale mismatch (common global
+ *    scale, ratio folded into the block scales, re-rounding error at most 6.2%) -- Japanese article,
+ *    "Trap 1"; the BF16 normalization layers ahead of the quantized projections -- Japanese article,
+ *    "Minima, quantized 'all 4-bit': the experiment design".
  *
  * Readings where the pages are silent:
  *  - every FP32 step is one IEEE binary32 operation rounded to nearest-even, in the order
@@ -279,6 +285,111 @@ void oracle_e2m1_from_float_array(const float* v, int64_t n, uint8_t* out) {
     double grid[8];
     e2m1_grid(grid);
     for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)nearest_even((double)v[i], grid, 8);
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Serving-path companions
+ * ---------------------------------------------------------------------------------------------- */
+
+/* bf16 round-to-nearest-even of a binary32 value (NaN -> canonical quiet NaN 0x7FC0). */
+static uint16_t bf16_from_float(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* E4M3FN byte of a finite binary32 value: sign bit kept, magnitude rounded to nearest-even with
+ * saturation at 448. NaN -> 0x7F. */
+static int e4m3_signed(float v, const double* grid) {
+    if (isnan(v)) return 0x7F;
+    int mag = nearest_even(fabs((double)v), grid, 127);
+    return (signbit(v) ? 0x80 : 0) | mag;
+}
+
+/* FP8 KV-cache scale, static per tensor, from a calibration amax: s = RN32(amax / 448), so that the
+ * largest calibrated magnitude maps to the top of the E4M3 range. */
+float oracle_kv_scale(float amax) { return amax / 448.0f; }
+
+/* FP8 KV-cache quantize: q = E4M3_RNE_SAT(RN32(x / s)) per element, x bf16 [rows, cols] with row
+ * stride ldx, q bytes with row stride ldq. Infinite inputs saturate to +-448, NaN gives 0x7F. */
+void oracle_kv_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float s, uint8_t* q,
+                        int64_t ldq) {
+    double grid[127];
+    e4m3_grid(grid);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float t = bf16_to_float(x[r * ldx + c]) / s;
+            q[r * ldq + c] = (uint8_t)e4m3_signed(t, grid);
+        }
+}
+
+/* FP8 KV-cache dequantize: y = bf16_RNE(RN32(e4m3(q) * s)); NaN codes give NaN. */
+void oracle_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s, uint16_t* y,
+                          int64_t ldy) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = (float)oracle_e4m3_value(q[r * ldq + c]); /* exact in binary32 (or NaN) */
+            y[r * ldy + c] = bf16_from_float(v * s);
+        }
+}
+
+/* Fold-in repair of a fused group (pages' own repair of the global-scale mismatch): the group is
+ * rewritten to one common global scale G and each module's ratio r = g / G is folded into its block
+ * scales: s' = E4M3_RNE_SAT(RN32(s * r)), codes unchanged. With G the group maximum (a reading: the
+ * pages do not say which common scale), r <= 1 and no folded scale can overflow 448. */
+float oracle_fold_common_scale(const float* g, int n) {
+    float G = 0.0f;
+    for (int i = 0; i < n; ++i)
+        if (g[i] > G) G = g[i];
+    return G;
+}
+
+float oracle_fold_ratio(float g, float G) { return g / G; }
+
+/* In place over a [rows, nblocks] scale array with row stride lds. The sign bit of a byte is kept
+ * and NaN bytes stay 0x7F. */
+void oracle_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, int64_t lds, float ratio) {
+    double grid[127];
+    e4m3_grid(grid);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nblocks; ++b) {
+            int byte = scales[r * lds + b];
+            double v = oracle_e4m3_value(byte);
+            if (isnan(v)) {
+                scales[r * lds + b] = 0x7F;
+                continue;
+            }
+            float t = (float)fabs(v) * ratio; /* RN32 */
+            scales[r * lds + b] = (uint8_t)((byte & 0x80) | nearest_even((double)t, grid, 127));
+        }
+}
+
+/* RMSNorm ahead of the quantizer, norm in BF16 (the pages keep normalization layers in BF16):
+ *   ms = (sum_k x_k^2) / K in double;  r = RN32(1 / sqrt(ms + eps)) (double, then one rounding);
+ *   y1_k = bf16_RNE(RN32(x_k * r));   y_k = bf16_RNE(y1_k * w_k)   (the product is exact in binary32).
+ * The two BF16 roundings follow the usual BF16 RMSNorm (normalize in FP32, round, scale by the
+ * weight); the pages do not spell the formula out. Also returns r per row. */
+void oracle_rmsnorm(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* w, float eps,
+                    uint16_t* y, int64_t ldy, float* r_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)bf16_to_float(x[i * ldx + k]);
+            ss += v * v;
+        }
+        double ms = ss / (double)K;
+        float r = (float)(1.0 / sqrt(ms + (double)eps));
+        if (r_out) r_out[i] = r;
+        for (int64_t k = 0; k < K; ++k) {
+            float y1 = bf16_to_float(bf16_from_float(bf16_to_float(x[i * ldx + k]) * r));
+            y[i * ldy + k] = bf16_from_float(y1 * bf16_to_float(w[k]));
+        }
+    }
 }
 
 /* Number of threads the OpenMP row loops use (1 without OpenMP). */
