@@ -15,6 +15,10 @@
  *      engineers should actually take away"), with an optional Gated DeltaNet gate epilogue
  *      (Japanese article, "Mechanism 2").
  *
+ * It also carries the companions of that layer on the same serving path: the FP8 E4M3 KV-cache
+ * codec with static scales, the pages' own fold-in repair of the scale mismatch, and BF16 RMSNorm
+ * fused with the quantizer (declared at the end of this file).
+ *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers; `stream` is a hipStream_t passed as void* (NULL means
  *    the null stream). Work is enqueued on `stream` and the call returns without synchronizing.
@@ -142,6 +146,86 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
 
 /* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none). */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------------------------------------
+ * Companions on the same serving path
+ * --------------------------------------------------------------------------------------------- */
+
+/*
+ * nvfp4_kv_scale -- static per-tensor FP8 KV-cache scale from a calibration tensor:
+ *   s = RN32(amax / 448), amax = max |x|, so that the calibrated maximum lands on the largest E4M3
+ *   value. The pages calibrate such scales offline and ship them with the checkpoint, one per K and
+ *   V tensor of each attention layer (Japanese article, "Is FP8 enough for the KV cache? The 'ship
+ *   KV scales' recipe"). Writes one float to the device pointer s_out (also used as the reduction
+ *   accumulator). x: device bf16 [rows, cols], stride ldx elements. Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float* s_out,
+                            void* stream);
+
+/*
+ * nvfp4_kv_quantize -- FP8 E4M3FN KV-cache quantization with a static scale (same passage):
+ *   q = E4M3_RNE_SAT(RN32(x / s)) per element: round to nearest even, saturating at +-448 (also
+ *   for infinities), sign kept (-0.0 and values rounding to zero give 0x80), NaN -> 0x7F.
+ *   x_bf16: device bf16 [rows, cols], stride ldx elements, 16-byte aligned, ldx % 8 == 0;
+ *   q: device uint8 [rows, cols], stride ldq bytes, 8-byte aligned, ldq % 8 == 0;
+ *   s: host float, finite and > 0. cols must be a multiple of 8. rows == 0 or cols == 0: no-op.
+ * Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
+ */
+nvfp4_status nvfp4_kv_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float s,
+                               uint8_t* q, int64_t ldq, void* stream);
+
+/*
+ * nvfp4_kv_dequantize -- FP8 E4M3FN KV-cache dequantization with the same static scale:
+ *   y = bf16_RNE(RN32(e4m3(q) * s)); NaN codes (0x7F, 0xFF) give the bf16 NaN 0x7FC0.
+ *   q: device uint8 [rows, cols], stride ldq bytes (8-byte aligned, ldq % 8 == 0);
+ *   y_bf16: device bf16 [rows, cols], stride ldy elements (16-byte aligned, ldy % 8 == 0).
+ * cols must be a multiple of 8. Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
+ */
+nvfp4_status nvfp4_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s,
+                                 void* y_bf16, int64_t ldy, void* stream);
+
+/*
+ * nvfp4_fold_scales -- the fold-in step of the pages' own repair of the fused-module scale mismatch
+ * (Japanese article, "Trap 1": the fused group is rewritten to one common global scale and each
+ * module's ratio is folded into its block scales, with a re-rounding error of at most 6.2%). In
+ * place over E4M3 scale bytes [rows, nblocks] (stride lds bytes):
+ *   s' = sign(s) | E4M3_RNE_SAT(RN32(|e4m3(s)| * ratio)); NaN bytes become 0x7F.
+ * For 0 < ratio <= 1 the relative re-rounding error is at most 2^-4 in the E4M3 normal range.
+ * ratio: host float, finite and > 0. Errors: NULL, SHAPE, SCALE, HIP.
+ */
+nvfp4_status nvfp4_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, int64_t lds, float ratio,
+                               void* stream);
+
+/*
+ * nvfp4_fold_group -- the whole fold-in repair of one fused weight tensor W [N, K] made of n_segs
+ * modules stacked along N (seg_rows[s] rows each, host array), with per-module global scales g_w
+ * (host array, finite, > 0): G = max_s g_w[s] (a reading: the pages do not name the common scale;
+ * the maximum keeps every ratio <= 1, so no folded scale overflows), r_s = RN32(g_w[s] / G), and
+ * nvfp4_fold_scales of module s's rows with r_s. Writes G to the host pointer g_common. Afterwards
+ * the group runs as one GEMM segment with global scale G (codes are unchanged).
+ *   w_scales: device uint8 [N, K/16], stride ldw_s bytes; K a multiple of 16.
+ * Errors: NULL, SHAPE, SEGMENTS, SCALE, HIP.
+ */
+nvfp4_status nvfp4_fold_group(uint8_t* w_scales, int64_t ldw_s, int64_t K, const int64_t* seg_rows,
+                              const float* g_w, int32_t n_segs, float* g_common, void* stream);
+
+/*
+ * nvfp4_rmsnorm_quantize -- BF16 RMSNorm fused with the NVFP4 quantizer of its output, so the
+ * normalized activations never go through HBM. The pages keep normalization layers in BF16
+ * (Japanese article, "Minima, quantized 'all 4-bit': the experiment design"); the formula below is
+ * the usual BF16 RMSNorm, which the pages do not spell out. Per row:
+ *   ms = (sum_k x_k^2) / K in double;  r = RN32(1 / sqrt(ms + eps)) (double, then one rounding);
+ *   y_k = bf16_RNE(bf16_RNE(RN32(x_k * r)) * w_k);   then y is quantized as by nvfp4_quantize.
+ *   x_bf16: device bf16 [rows, K], stride ldx;  w_bf16: device bf16 [K] (16-byte aligned);
+ *   eps: host float >= 0;  g: host float global scale of the consuming module (finite, > 0);
+ *   codes/scales: as nvfp4_quantize;  y_bf16: optional device bf16 [rows, K] (stride ldy) that also
+ *   receives y, or NULL.
+ * K must be a multiple of 16. Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
+ */
+nvfp4_status nvfp4_rmsnorm_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx,
+                                    const void* w_bf16, float eps, float g, uint8_t* codes, int64_t ldc,
+                                    uint8_t* scales, int64_t lds, void* y_bf16, int64_t ldy,
+                                    void* stream);
 
 /* Static English name of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);

@@ -2,7 +2,9 @@
 
 Argument marshalling only: every step of the path runs in the library's HIP kernels. PyTorch is
 used for device memory and the current stream. The names mirror the C interface in
-include/nvfp4.h (nvfp4_global_scale, nvfp4_quantize, nvfp4_gemm).
+include/nvfp4.h (nvfp4_global_scale, nvfp4_quantize, nvfp4_gemm, and the serving-path companions
+nvfp4_kv_scale / nvfp4_kv_quantize / nvfp4_kv_dequantize, nvfp4_fold_scales / nvfp4_fold_group,
+nvfp4_rmsnorm_quantize).
 
 If the library has not been built (``python -m nvfp4_w4a4_quantized_quantize_amd.build``), every
 call raises: there is no fallback implementation.
@@ -27,7 +29,8 @@ _EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
 
 # Every function the C header declares; a test checks the library exports all of them.
 EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
-            "nvfp4_status_string", "nvfp4_last_error")
+            "nvfp4_status_string", "nvfp4_last_error", "nvfp4_kv_scale", "nvfp4_kv_quantize",
+            "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize")
 
 
 class Nvfp4Error(RuntimeError):
@@ -66,6 +69,19 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_status_string.argtypes = [i32]
         L.nvfp4_last_error.restype = ctypes.c_char_p
         L.nvfp4_last_error.argtypes = []
+        L.nvfp4_kv_scale.restype = i32
+        L.nvfp4_kv_scale.argtypes = [P, i64, i64, i64, P, P]
+        L.nvfp4_kv_quantize.restype = i32
+        L.nvfp4_kv_quantize.argtypes = [P, i64, i64, i64, f32, P, i64, P]
+        L.nvfp4_kv_dequantize.restype = i32
+        L.nvfp4_kv_dequantize.argtypes = [P, i64, i64, i64, f32, P, i64, P]
+        L.nvfp4_fold_scales.restype = i32
+        L.nvfp4_fold_scales.argtypes = [P, i64, i64, i64, f32, P]
+        L.nvfp4_fold_group.restype = i32
+        L.nvfp4_fold_group.argtypes = [P, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(f32), i32,
+                                       ctypes.POINTER(f32), P]
+        L.nvfp4_rmsnorm_quantize.restype = i32
+        L.nvfp4_rmsnorm_quantize.argtypes = [P, i64, i64, i64, P, f32, f32, P, i64, P, i64, P, i64, P]
         _lib = L
     return _lib
 
@@ -185,3 +201,77 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: tor
                             _ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), M, N, K,
                             segs, g_w, n_segs, _ptr(workspace), ws_bytes, _stream(stream)), "nvfp4_gemm")
     return outs
+
+
+# ------------------------------------------------------------------------ FP8 E4M3 KV-cache codec
+def kv_scale(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Static KV scale s = RN32(max|x| / 448) of a bf16 [rows, cols] calibration tensor (float32 [1])."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_kv_scale(_ptr(x), x.shape[0], x.shape[1], _ld(x, 8), _ptr(out), _stream(stream)),
+           "nvfp4_kv_scale")
+    return out
+
+
+def kv_quantize(x: torch.Tensor, s: float, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q = E4M3_RNE_SAT(RN32(x / s)) of a bf16 [rows, cols] tensor, as uint8 [rows, cols]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_kv_quantize(_ptr(x), x.shape[0], x.shape[1], _ld(x, 8), float(s), _ptr(out), _ld(out, 8),
+                                   _stream(stream)), "nvfp4_kv_quantize")
+    return out
+
+
+def kv_dequantize(q: torch.Tensor, s: float, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = bf16_RNE(RN32(e4m3(q) * s)) of uint8 E4M3 codes [rows, cols], as bf16 [rows, cols]."""
+    assert q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check(lib().nvfp4_kv_dequantize(_ptr(q), q.shape[0], q.shape[1], _ld(q, 8), float(s), _ptr(out), _ld(out, 8),
+                                     _stream(stream)), "nvfp4_kv_dequantize")
+    return out
+
+
+# ----------------------------------------------------------------------------- fold-in repair
+def fold_scales(scales: torch.Tensor, ratio: float, stream=None) -> torch.Tensor:
+    """In place: s' = E4M3_RNE_SAT(RN32(s * ratio)) over uint8 E4M3 scales [rows, nblocks]."""
+    assert scales.dtype == torch.uint8 and scales.dim() == 2 and scales.stride(1) == 1
+    _check(lib().nvfp4_fold_scales(_ptr(scales), scales.shape[0], scales.shape[1], _ld(scales, 1), float(ratio),
+                                   _stream(stream)), "nvfp4_fold_scales")
+    return scales
+
+
+def fold_group(w_scales: torch.Tensor, seg_rows: Sequence[int], g_w: Sequence[float], stream=None) -> float:
+    """In place fold-in repair of a fused weight's scales [N, K/16]; returns the common scale G."""
+    assert w_scales.dtype == torch.uint8 and w_scales.dim() == 2 and w_scales.stride(1) == 1
+    n = len(seg_rows)
+    rows = (ctypes.c_int64 * max(n, 1))(*seg_rows)
+    gs = (ctypes.c_float * max(n, 1))(*[float(g) for g in g_w])
+    G = ctypes.c_float(0.0)
+    _check(lib().nvfp4_fold_group(_ptr(w_scales), _ld(w_scales, 16), w_scales.shape[1] * 16, rows, gs, n,
+                                  ctypes.byref(G), _stream(stream)), "nvfp4_fold_group")
+    return G.value
+
+
+# ----------------------------------------------------------------------- RMSNorm + quantize
+def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, g: float, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, stream=None):
+    """BF16 RMSNorm of x [rows, K] with weight w [K], quantized to NVFP4 with global scale g.
+
+    Returns (codes, scales); when y (bf16 [rows, K]) is given it also receives the normalized rows.
+    """
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert w.dtype == torch.bfloat16 and w.dim() == 1 and w.stride(0) == 1 and w.shape[0] == x.shape[1]
+    rows, K = x.shape
+    if codes is None or scales is None:
+        codes, scales = alloc_nvfp4(rows, K, x.device)
+    ldy = 0
+    if y is not None:
+        assert y.dtype == torch.bfloat16 and y.shape == x.shape and y.stride(1) == 1
+        ldy = _ld(y, 8)
+    _check(lib().nvfp4_rmsnorm_quantize(_ptr(x), rows, K, _ld(x, 8), _ptr(w), float(eps), float(g), _ptr(codes),
+                                        _ld(codes, 16), _ptr(scales), _ld(scales, 16), _ptr(y), ldy,
+                                        _stream(stream)), "nvfp4_rmsnorm_quantize")
+    return codes, scales

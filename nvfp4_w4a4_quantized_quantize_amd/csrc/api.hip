@@ -90,8 +90,8 @@ nvfp4_status nvfp4_global_scale(const void* x_bf16, int64_t rows, int64_t K, int
     if (st != NVFP4_OK) return st;
     if (!g_out) return fail(NVFP4_ERR_NULL, "g_out is NULL");
     if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(NVFP4_ERR_ALIGN, "g_out must be 4-byte aligned");
-    return hip_status(nvfp4::launch_global_scale(static_cast<const uint16_t*>(x_bf16), rows, K, ldx, g_out,
-                                                 static_cast<hipStream_t>(stream)),
+    return hip_status(nvfp4::launch_amax_scale(static_cast<const uint16_t*>(x_bf16), rows, K, ldx, 6.0f * 448.0f,
+                                               g_out, static_cast<hipStream_t>(stream)),
                       "nvfp4_global_scale launch");
 }
 
@@ -176,6 +176,117 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     return hip_status(launch(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
                              static_cast<hipStream_t>(stream)),
                       "nvfp4_gemm launch");
+}
+
+nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float* s_out,
+                            void* stream) {
+    nvfp4_status st = check_bf16_matrix(x_bf16, rows, cols, ldx, "x");
+    if (st != NVFP4_OK) return st;
+    if (!s_out) return fail(NVFP4_ERR_NULL, "s_out is NULL");
+    if ((reinterpret_cast<uintptr_t>(s_out) & 3u) != 0) return fail(NVFP4_ERR_ALIGN, "s_out must be 4-byte aligned");
+    return hip_status(nvfp4::launch_amax_scale(static_cast<const uint16_t*>(x_bf16), rows, cols, ldx, 448.0f, s_out,
+                                               static_cast<hipStream_t>(stream)),
+                      "nvfp4_kv_scale launch");
+}
+
+namespace {
+
+// An FP8 byte matrix [rows, cols] with stride ldq: 8-byte aligned base and stride.
+nvfp4_status check_fp8_matrix(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const char* name) {
+    if (rows == 0 || cols == 0) return NVFP4_OK;
+    if (!q) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
+    if (ldq < cols) return fail(NVFP4_ERR_SHAPE, "%s: row stride %lld < cols = %lld", name, (long long)ldq, (long long)cols);
+    if ((reinterpret_cast<uintptr_t>(q) & 7u) != 0 || ldq % 8 != 0)
+        return fail(NVFP4_ERR_ALIGN, "%s: base must be 8-byte aligned and the row stride a multiple of 8", name);
+    return NVFP4_OK;
+}
+
+nvfp4_status check_kv_shape(int64_t rows, int64_t cols, float s) {
+    if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (cols % 8 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 8", (long long)cols);
+    if (!good_scale(s)) return fail(NVFP4_ERR_SCALE, "KV scale s = %g must be finite and > 0", (double)s);
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_kv_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float s, uint8_t* q,
+                               int64_t ldq, void* stream) {
+    nvfp4_status st = check_kv_shape(rows, cols, s);
+    if (st != NVFP4_OK) return st;
+    if ((st = check_bf16_matrix(x_bf16, rows, cols, ldx, "x")) != NVFP4_OK) return st;
+    if ((st = check_fp8_matrix(q, rows, cols, ldq, "q")) != NVFP4_OK) return st;
+    if (rows == 0 || cols == 0) return ok();
+    return hip_status(nvfp4::launch_kv_quantize(static_cast<const uint16_t*>(x_bf16), rows, cols, ldx, s, q, ldq,
+                                                static_cast<hipStream_t>(stream)),
+                      "nvfp4_kv_quantize launch");
+}
+
+nvfp4_status nvfp4_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s, void* y_bf16,
+                                 int64_t ldy, void* stream) {
+    nvfp4_status st = check_kv_shape(rows, cols, s);
+    if (st != NVFP4_OK) return st;
+    if ((st = check_fp8_matrix(q, rows, cols, ldq, "q")) != NVFP4_OK) return st;
+    if ((st = check_bf16_matrix(y_bf16, rows, cols, ldy, "y")) != NVFP4_OK) return st;
+    if (rows == 0 || cols == 0) return ok();
+    return hip_status(nvfp4::launch_kv_dequantize(q, rows, cols, ldq, s, static_cast<uint16_t*>(y_bf16), ldy,
+                                                  static_cast<hipStream_t>(stream)),
+                      "nvfp4_kv_dequantize launch");
+}
+
+nvfp4_status nvfp4_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, int64_t lds, float ratio,
+                               void* stream) {
+    if (rows < 0 || nblocks < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (!good_scale(ratio)) return fail(NVFP4_ERR_SCALE, "ratio = %g must be finite and > 0", (double)ratio);
+    if (rows == 0 || nblocks == 0) return ok();
+    if (!scales) return fail(NVFP4_ERR_NULL, "scales is NULL");
+    if (lds < nblocks) return fail(NVFP4_ERR_SHAPE, "row stride %lld < nblocks = %lld", (long long)lds, (long long)nblocks);
+    return hip_status(nvfp4::launch_fold_scales(scales, rows, nblocks, lds, ratio, static_cast<hipStream_t>(stream)),
+                      "nvfp4_fold_scales launch");
+}
+
+nvfp4_status nvfp4_fold_group(uint8_t* w_scales, int64_t ldw_s, int64_t K, const int64_t* seg_rows, const float* g_w,
+                              int32_t n_segs, float* g_common, void* stream) {
+    if (!seg_rows || !g_w || !g_common) return fail(NVFP4_ERR_NULL, "seg_rows, g_w or g_common is NULL");
+    if (K < 0 || K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a non-negative multiple of 16", (long long)K);
+    if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
+        return fail(NVFP4_ERR_SEGMENTS, "n_segs = %d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);
+    float G = 0.0f;
+    for (int s = 0; s < n_segs; ++s) {
+        if (seg_rows[s] < 0) return fail(NVFP4_ERR_SEGMENTS, "segment %d has %lld rows", s, (long long)seg_rows[s]);
+        if (!good_scale(g_w[s])) return fail(NVFP4_ERR_SCALE, "g_w[%d] = %g must be finite and > 0", s, (double)g_w[s]);
+        if (g_w[s] > G) G = g_w[s];
+    }
+    *g_common = G;
+    int64_t row0 = 0;
+    for (int s = 0; s < n_segs; ++s) {
+        const float ratio = g_w[s] / G;  // RN32
+        nvfp4_status st = nvfp4_fold_scales(w_scales + row0 * ldw_s, seg_rows[s], K / 16, ldw_s, ratio, stream);
+        if (st != NVFP4_OK) return st;
+        row0 += seg_rows[s];
+    }
+    return ok();
+}
+
+nvfp4_status nvfp4_rmsnorm_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx, const void* w_bf16,
+                                    float eps, float g, uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                                    void* y_bf16, int64_t ldy, void* stream) {
+    if (rows < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+    nvfp4_status st = check_bf16_matrix(x_bf16, rows, K, ldx, "x");
+    if (st != NVFP4_OK) return st;
+    if ((st = check_nvfp4(codes, ldc, scales, lds, rows, K, "output")) != NVFP4_OK) return st;
+    if (y_bf16 && (st = check_bf16_matrix(y_bf16, rows, K, ldy, "y")) != NVFP4_OK) return st;
+    if (!good_scale(g)) return fail(NVFP4_ERR_SCALE, "global scale g = %g must be finite and > 0", (double)g);
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(NVFP4_ERR_SCALE, "eps = %g must be finite and >= 0", (double)eps);
+    if (rows == 0 || K == 0) return ok();
+    if (!w_bf16) return fail(NVFP4_ERR_NULL, "w is NULL");
+    if (!aligned16(w_bf16)) return fail(NVFP4_ERR_ALIGN, "w must be 16-byte aligned");
+    return hip_status(nvfp4::launch_rmsnorm_quantize(static_cast<const uint16_t*>(x_bf16), rows, K, ldx,
+                                                     static_cast<const uint16_t*>(w_bf16), eps, g, codes, ldc, scales,
+                                                     lds, static_cast<uint16_t*>(y_bf16), ldy,
+                                                     static_cast<hipStream_t>(stream)),
+                      "nvfp4_rmsnorm_quantize launch");
 }
 
 }  // extern "C"

@@ -25,8 +25,9 @@ struct SegParams {
 };
 
 // Launchers: shapes are validated by the C interface before these are called.
-hipError_t launch_global_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float* g_out,
-                               hipStream_t stream);
+// Writes RN32(max |x| / divisor) to the device float g_out.
+hipError_t launch_amax_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float divisor,
+                             float* g_out, hipStream_t stream);
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float g,
                            uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
                            hipStream_t stream);
@@ -41,5 +42,15 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                               int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+
+hipError_t launch_kv_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float s, uint8_t* q,
+                              int64_t ldq, hipStream_t stream);
+hipError_t launch_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s, uint16_t* y,
+                                int64_t ldy, hipStream_t stream);
+hipError_t launch_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, int64_t lds, float ratio,
+                              hipStream_t stream);
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* w,
+                                   float eps, float g, uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                                   uint16_t* y, int64_t ldy, hipStream_t stream);
 
 }  // namespace nvfp4

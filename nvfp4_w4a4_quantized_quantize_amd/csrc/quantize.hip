@@ -10,34 +10,13 @@
 // Every rounding decision is taken in IEEE binary32 exactly as specified:
 //   t = RN32(6 g); s = E4M3_RNE_SAT(RN32(amax / t)); S = RN32(s g); v = RN32(|x| / S);
 //   code = sign(x) | E2M1_RNE_SAT(v).
-#include "internal.h"
+#include "quant_common.h"
 
 namespace nvfp4 {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// E4M3FN round-to-nearest-even with saturation at 448. The gfx950 conversion rounds to nearest
-// even in the OCP E4M3FN format but turns inputs of 464 and above into NaN, so clamp first.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-    v = fminf(v, 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
-}
-
-__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
-}
-
-// Two signed E2M1 codes (round to nearest even, saturating at 6, sign kept for zero) into byte
-// `sel` of `word`: the first value goes to the low nibble.
-template <int sel>
-__device__ __forceinline__ uint32_t put_e2m1_pair(uint32_t word, float lo, float hi) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lo, hi, 1.0f, sel);
-}
+typedef qu32x4 u32x4;
+typedef qu32x2 u32x2;
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                        uint8_t* __restrict__ codes, int64_t ldc,
@@ -63,54 +42,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         f[2 * i] = bf16_lo(w[i]);
         f[2 * i + 1] = bf16_hi(w[i]);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-
-    const float t = 6.0f * g;
-    const float s_raw = __fdiv_rn(amax, t);
-    const uint32_t sb = e4m3_rne_sat(s_raw);
-    const float s = e4m3_to_f32(sb);
-    const float S = s * g;
-
-    // v = RN32(|x| / S). Fast path: y = rcp(S) then one exact-residual correction
-    //   q0 = |x| y;  r = fma(-q0, S, |x|) (exact);  q1 = fma(r, y, q0)
-    // which equals the correctly rounded quotient for bf16 |x| whenever S, 1/S and the quotient
-    // stay inside the normal range (checked against IEEE division for every bf16 significand and
-    // every binary32 significand of S). A zero scale takes y = 0, giving q1 = 0. Blocks outside
-    // that range (extreme global scales) use the IEEE division.
-    const bool fast = (s == 0.0f) || (S >= 0x1p-100f && S <= 0x1p100f && amax * 0x1p-100f <= S);
-    float v[16];
-    if (fast) {
-        const float y = (s == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(S);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float a = fabsf(f[i]);
-            const float q0 = a * y;
-            const float r = __builtin_fmaf(-q0, S, a);
-            const float q1 = __builtin_fmaf(r, y, q0);
-            v[i] = __builtin_copysignf(q1, f[i]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(__fdiv_rn(fabsf(f[i]), S), f[i]);
-    }
-    uint32_t c0 = 0, c1 = 0;
-    c0 = put_e2m1_pair<0>(c0, v[0], v[1]);
-    c0 = put_e2m1_pair<1>(c0, v[2], v[3]);
-    c0 = put_e2m1_pair<2>(c0, v[4], v[5]);
-    c0 = put_e2m1_pair<3>(c0, v[6], v[7]);
-    c1 = put_e2m1_pair<0>(c1, v[8], v[9]);
-    c1 = put_e2m1_pair<1>(c1, v[10], v[11]);
-    c1 = put_e2m1_pair<2>(c1, v[12], v[13]);
-    c1 = put_e2m1_pair<3>(c1, v[14], v[15]);
+    const Block16 q = encode_block16(f, g);
 
     u32x2* dst = reinterpret_cast<u32x2*>(codes + row * ldc + (uint64_t)b * 8u);
-    __builtin_nontemporal_store(u32x2{c0, c1}, dst);
-    scales[row * lds + b] = (uint8_t)sb;
+    __builtin_nontemporal_store(u32x2{q.c0, q.c1}, dst);
+    scales[row * lds + b] = (uint8_t)q.sb;
 }
 
-// ---- global scale: g = RN32(amax / 2688) ------------------------------------------------------
+// ---- scale from a tensor amax: RN32(amax / divisor) (2688 = 6 * 448 for NVFP4, 448 for FP8 KV) ----
 __global__ void clear_word_kernel(uint32_t* p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0u;
 }
@@ -136,24 +75,24 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
     if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(acc, __float_as_uint(m));
 }
 
-__global__ void finish_scale_kernel(float* g_out) {
+__global__ void finish_scale_kernel(float* g_out, float divisor) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         const float amax = __uint_as_float(*reinterpret_cast<uint32_t*>(g_out));
-        *g_out = __fdiv_rn(amax, 6.0f * 448.0f);
+        *g_out = __fdiv_rn(amax, divisor);
     }
 }
 
 }  // namespace
 
-hipError_t launch_global_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float* g_out,
-                               hipStream_t stream) {
+hipError_t launch_amax_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, float divisor,
+                             float* g_out, hipStream_t stream) {
     uint32_t* acc = reinterpret_cast<uint32_t*>(g_out);
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, acc);
     if (rows > 0 && K > 0) {
         const int64_t grid = rows < 8192 ? rows : 8192;
         hipLaunchKernelGGL(amax_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, rows, K, ldx, acc);
     }
-    hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(64), 0, stream, g_out);
+    hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(64), 0, stream, g_out, divisor);
     return hipGetLastError();
 }
 

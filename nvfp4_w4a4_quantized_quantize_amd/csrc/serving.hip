@@ -1,0 +1,227 @@
+// Companions of the NVFP4 linear layer on the same serving path, for gfx950 (CDNA4):
+//  * FP8 E4M3 KV-cache codec with static per-tensor scales, calibrated offline and shipped with the
+//    checkpoint (paper arXiv:2609.04098; Japanese article, "Is FP8 enough for the KV cache? The 'ship
+//    KV scales' recipe"): q = E4M3_RNE_SAT(RN32(x / s)), x^ = bf16_RNE(RN32(e4m3(q) s)).
+//  * The fold-in repair of the fused-module global-scale mismatch (Japanese article, "Trap 1"): the
+//    fused group takes one common global scale G and each module's ratio r = g / G is folded into
+//    its block scales, s' = E4M3_RNE_SAT(RN32(s r)); codes are unchanged.
+//  * BF16 RMSNorm fused with the NVFP4 quantizer of its output (the pages keep normalization layers
+//    in BF16; Japanese article, experiment design), so the normalized activations never go to HBM.
+// All three are streaming kernels bound by HBM bandwidth.
+#include <cmath>
+
+#include "quant_common.h"
+
+namespace nvfp4 {
+namespace {
+
+// RN32(a / S) for a = |x| of a bf16 value, S > 0: the reciprocal with one exact-residual correction
+// is the correctly rounded quotient while S, 1/S and the quotient stay in the normal range (the
+// condition the NVFP4 block encoder uses); otherwise the IEEE division.
+__device__ __forceinline__ float quotient_rn(float a, float S, float y, bool s_ok) {
+    if (s_ok && a * 0x1p-100f <= S) {
+        const float q0 = a * y;
+        const float r = __builtin_fmaf(-q0, S, a);
+        return __builtin_fmaf(r, y, q0);
+    }
+    return __fdiv_rn(a, S);
+}
+
+// One signed E4M3FN byte: saturating round to nearest even, sign kept, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_signed(float q, float xsign) {
+    if (q != q) return 0x7Fu;
+    const uint32_t mag = e4m3_rne_sat(q);  // q >= 0 here
+    return (__float_as_uint(xsign) >> 24 & 0x80u) | mag;
+}
+
+// ---- FP8 KV codec: one thread = 8 consecutive elements ----------------------------------------
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                          uint8_t* __restrict__ q, int64_t ldq, float s,
+                                                          uint32_t units, uint32_t blocks_per_row) {
+    const uint32_t row = blockIdx.x / blocks_per_row;
+    const uint32_t u = (blockIdx.x - row * blocks_per_row) * 256u + threadIdx.x;
+    if (u >= units) return;
+    const qu32x4 p = __builtin_nontemporal_load(reinterpret_cast<const qu32x4*>(x + (int64_t)row * ldx + 8u * u));
+    const float y = __builtin_amdgcn_rcpf(s);
+    const bool s_ok = s >= 0x1p-100f && s <= 0x1p100f;
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w = p[2 * h + i];
+            const float f0 = bf16_lo(w), f1 = bf16_hi(w);
+            const uint32_t b0 = e4m3_signed(quotient_rn(fabsf(f0), s, y, s_ok), f0);
+            const uint32_t b1 = e4m3_signed(quotient_rn(fabsf(f1), s, y, s_ok), f1);
+            word |= (b0 | (b1 << 8)) << (16 * i);
+        }
+        out[h] = word;
+    }
+    __builtin_nontemporal_store(qu32x2{out[0], out[1]}, reinterpret_cast<qu32x2*>(q + (int64_t)row * ldq + 8u * u));
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+    if (v != v) return 0x7FC0u;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__global__ __launch_bounds__(256) void kv_dequantize_kernel(const uint8_t* __restrict__ q, int64_t ldq,
+                                                            uint16_t* __restrict__ y, int64_t ldy, float s,
+                                                            uint32_t units, uint32_t blocks_per_row) {
+    const uint32_t row = blockIdx.x / blocks_per_row;
+    const uint32_t u = (blockIdx.x - row * blocks_per_row) * 256u + threadIdx.x;
+    if (u >= units) return;
+    const qu32x2 p = __builtin_nontemporal_load(reinterpret_cast<const qu32x2*>(q + (int64_t)row * ldq + 8u * u));
+    qu32x4 o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int w = (int)p[h];
+        const float v0 = __builtin_amdgcn_cvt_f32_fp8(w, 0) * s;
+        const float v1 = __builtin_amdgcn_cvt_f32_fp8(w, 1) * s;
+        const float v2 = __builtin_amdgcn_cvt_f32_fp8(w, 2) * s;
+        const float v3 = __builtin_amdgcn_cvt_f32_fp8(w, 3) * s;
+        o[2 * h] = bf16_bits_rne(v0) | (bf16_bits_rne(v1) << 16);
+        o[2 * h + 1] = bf16_bits_rne(v2) | (bf16_bits_rne(v3) << 16);
+    }
+    __builtin_nontemporal_store(o, reinterpret_cast<qu32x4*>(y + (int64_t)row * ldy + 8u * u));
+}
+
+// ---- fold-in repair: one thread = one scale byte, in place -------------------------------------
+__global__ __launch_bounds__(256) void fold_scales_kernel(uint8_t* __restrict__ scales, int64_t lds, float ratio,
+                                                          uint32_t nblocks, uint32_t blocks_per_row) {
+    const uint32_t row = blockIdx.x / blocks_per_row;
+    const uint32_t b = (blockIdx.x - row * blocks_per_row) * 256u + threadIdx.x;
+    if (b >= nblocks) return;
+    uint8_t* p = scales + (int64_t)row * lds + b;
+    const uint32_t byte = *p;
+    uint32_t out = 0x7Fu;
+    if ((byte & 0x7Fu) != 0x7Fu) out = (byte & 0x80u) | e4m3_rne_sat(e4m3_to_f32(byte & 0x7Fu) * ratio);
+    *p = (uint8_t)out;
+}
+
+// ---- RMSNorm + NVFP4 quantize: one wave = one row ----------------------------------------------
+//   ms = sum(x^2) / K in double; r = RN32(1 / sqrt(ms + eps)) (double, then one rounding);
+//   y1 = bf16_RNE(RN32(x r)); y = bf16_RNE(y1 w) (the product of two bf16 values is exact in FP32);
+//   then y is encoded as NVFP4 with the static global scale g.
+// The row is read twice: the second pass finds it in L2, so HBM sees it once.
+__global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* __restrict__ w, float eps,
+    float g, uint8_t* __restrict__ codes, int64_t ldc, uint8_t* __restrict__ scales, int64_t lds,
+    uint16_t* __restrict__ y_out, int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t nb = K / 16;
+    const uint16_t* xr = x + row * ldx;
+
+    double ss = 0.0;
+    for (int64_t b = lane; b < nb; b += 64) {
+        const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
+        const qu32x4 p0 = src[0], p1 = src[1];
+        const uint32_t wv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double lo = bf16_lo(wv[i]), hi = bf16_hi(wv[i]);
+            ss += lo * lo;
+            ss += hi * hi;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const double ms = __ddiv_rn(ss, (double)K);
+    const float r = (float)__ddiv_rn(1.0, __dsqrt_rn(ms + (double)eps));
+
+    for (int64_t b = lane; b < nb; b += 64) {
+        const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
+        const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
+        const qu32x4 p0 = src[0], p1 = src[1], w0 = wsrc[0], w1 = wsrc[1];
+        const uint32_t xv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float y1lo = (float)(__bf16)(bf16_lo(xv[i]) * r);
+            const float y1hi = (float)(__bf16)(bf16_hi(xv[i]) * r);
+            f[2 * i] = (float)(__bf16)(y1lo * bf16_lo(wv[i]));
+            f[2 * i + 1] = (float)(__bf16)(y1hi * bf16_hi(wv[i]));
+        }
+        const Block16 q = encode_block16(f, g);
+        *reinterpret_cast<qu32x2*>(codes + row * ldc + 8 * b) = qu32x2{q.c0, q.c1};
+        scales[row * lds + b] = (uint8_t)q.sb;
+        if (y_out) {
+            qu32x4 o0, o1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o0[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+                o1[i] = (__float_as_uint(f[8 + 2 * i]) >> 16) | (__float_as_uint(f[8 + 2 * i + 1]) & 0xffff0000u);
+            }
+            qu32x4* dst = reinterpret_cast<qu32x4*>(y_out + row * ldy + 16 * b);
+            dst[0] = o0;
+            dst[1] = o1;
+        }
+    }
+}
+
+// Rows of `units` work items (256 per block): returns false when the grid would not fit one launch.
+bool row_grid(int64_t rows, int64_t units, uint32_t* blocks_per_row, uint32_t* grid) {
+    const int64_t bpr = (units + 255) / 256;
+    if (units > 0xFFFFFFFFll || bpr == 0 || rows * bpr > 0x7FFFFFFFll) return false;
+    *blocks_per_row = (uint32_t)bpr;
+    *grid = (uint32_t)(rows * bpr);
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_kv_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float s, uint8_t* q,
+                              int64_t ldq, hipStream_t stream) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (ldx == cols && ldq == cols) {  // contiguous: one long row
+        cols *= rows;
+        rows = 1;
+    }
+    uint32_t bpr, grid;
+    if (!row_grid(rows, cols / 8, &bpr, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kv_quantize_kernel, dim3(grid), dim3(256), 0, stream, x, ldx, q, ldq, s, (uint32_t)(cols / 8), bpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s, uint16_t* y,
+                                int64_t ldy, hipStream_t stream) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (ldq == cols && ldy == cols) {
+        cols *= rows;
+        rows = 1;
+    }
+    uint32_t bpr, grid;
+    if (!row_grid(rows, cols / 8, &bpr, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kv_dequantize_kernel, dim3(grid), dim3(256), 0, stream, q, ldq, y, ldy, s, (uint32_t)(cols / 8), bpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, int64_t lds, float ratio,
+                              hipStream_t stream) {
+    if (rows == 0 || nblocks == 0) return hipSuccess;
+    if (lds == nblocks) {
+        nblocks *= rows;
+        rows = 1;
+    }
+    uint32_t bpr, grid;
+    if (!row_grid(rows, nblocks, &bpr, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fold_scales_kernel, dim3(grid), dim3(256), 0, stream, scales, lds, ratio, (uint32_t)nblocks, bpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* w,
+                                   float eps, float g, uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
+                                   uint16_t* y, int64_t ldy, hipStream_t stream) {
+    if (rows == 0 || K == 0) return hipSuccess;
+    const int64_t grid = (rows + 3) / 4;
+    if (grid > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(rmsnorm_quantize_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, rows, K, ldx, w, eps,
+                       g, codes, ldc, scales, lds, y, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

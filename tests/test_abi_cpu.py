@@ -116,3 +116,65 @@ def test_gemm_rejects(L, kw, status):
 def test_gemm_empty_shapes_ok_without_launch(L):
     assert g(L, M=0) == 0
     assert g(L, N=0, segs=[(0, 0, 0, 0, A16, 0, None, None)], n_segs=0) == 4  # still needs one segment
+
+
+# --------------------------------------------------------------- serving-path companions
+def kvq(L, x=A16, rows=4, cols=64, ldx=64, s=0.5, q=A16, ldq=64):
+    return L.nvfp4_kv_quantize(x, rows, cols, ldx, s, q, ldq, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(q=None), 1),
+    (dict(cols=60, ldx=64, ldq=64), 2), (dict(rows=-1), 2), (dict(ldx=56), 2), (dict(ldq=32), 2),
+    (dict(x=A16 + 8), 3), (dict(ldx=68), 3), (dict(q=A16 + 4), 3), (dict(ldq=68), 3),
+    (dict(s=0.0), 5), (dict(s=float("nan")), 5), (dict(s=float("inf")), 5),
+])
+def test_kv_quantize_rejects(L, kw, status):
+    assert kvq(L, **kw) == status
+    assert nv.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(y=None), 1), (dict(cols=12, ldq=16, ldy=16), 2), (dict(y=A16 + 2), 3),
+    (dict(q=A16 + 1), 3), (dict(s=-2.0), 5),
+])
+def test_kv_dequantize_rejects(L, kw, status):
+    a = dict(q=A16, rows=4, cols=64, ldq=64, s=0.5, y=A16, ldy=64)
+    a.update(kw)
+    assert L.nvfp4_kv_dequantize(a["q"], a["rows"], a["cols"], a["ldq"], a["s"], a["y"], a["ldy"], None) == status
+
+
+def test_kv_empty_and_scale_rejects(L):
+    assert kvq(L, rows=0) == 0 and kvq(L, cols=0, ldx=0, ldq=0) == 0
+    assert L.nvfp4_kv_scale(A16, 4, 64, 64, None, None) == 1
+    assert L.nvfp4_kv_scale(A16, 4, 64, 64, A16 + 2, None) == 3
+
+
+def test_fold_rejects(L):
+    assert L.nvfp4_fold_scales(None, 4, 8, 16, 0.5, None) == 1
+    assert L.nvfp4_fold_scales(A16, 4, 8, 4, 0.5, None) == 2
+    assert L.nvfp4_fold_scales(A16, 4, 8, 16, 0.0, None) == 5
+    assert L.nvfp4_fold_scales(A16, 0, 8, 16, 0.5, None) == 0
+    rows = (ctypes.c_int64 * 2)(4, 4)
+    gw = (ctypes.c_float * 2)(0.5, 1.0)
+    G = ctypes.c_float(0)
+    assert L.nvfp4_fold_group(A16, 16, 64, rows, gw, 0, ctypes.byref(G), None) == 4
+    assert L.nvfp4_fold_group(A16, 16, 60, rows, gw, 2, ctypes.byref(G), None) == 2
+    bad = (ctypes.c_float * 2)(0.5, float("nan"))
+    assert L.nvfp4_fold_group(A16, 16, 64, rows, bad, 2, ctypes.byref(G), None) == 5
+    assert L.nvfp4_fold_group(A16, 16, 64, rows, gw, 2, None, None) == 1
+
+
+def rq(L, x=A16, rows=4, K=64, ldx=64, w=A16, eps=1e-6, g=1.0, codes=A16, ldc=32, scales=A16, lds=16, y=None,
+       ldy=0):
+    return L.nvfp4_rmsnorm_quantize(x, rows, K, ldx, w, eps, g, codes, ldc, scales, lds, y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(codes=None), 1),
+    (dict(K=24, ldx=32), 2), (dict(y=A16, ldy=32), 2),
+    (dict(w=A16 + 2), 3), (dict(x=A16 + 8), 3), (dict(y=A16 + 8, ldy=64), 3),
+    (dict(g=0.0), 5), (dict(eps=-1.0), 5), (dict(eps=float("nan")), 5),
+])
+def test_rmsnorm_quantize_rejects(L, kw, status):
+    assert rq(L, **kw) == status
