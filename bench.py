@@ -223,12 +223,149 @@ def run_cpu_baseline(step: Step, rows_quant: int, rows_gemm: int) -> dict:
     }
 
 
+# ----------------------------------------------------------------------- serving-path companions
+COMPANIONS = ("kv_cache", "rmsnorm_quantize")
+
+
+def _time_loop(fn, n: int) -> float:
+    """Milliseconds per call of fn(i) over n back-to-back calls on the current stream (HIP events)."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def bench_kv_cache(steps: int, warmup: int, cpu: bool) -> dict:
+    """One step = the FP8 KV-cache write of a 32K-token prefill for every attention layer (K and V
+    of 16 layers, each quantized with its own static scale), then the read of all of it back to
+    bf16. Layer l's tensors are the two seeded base draws times 2^(l/4 - 2) (rounded to bf16), so
+    the 32 tensors (3.2 GB with their codes) stream from HBM."""
+    import oracle
+    case = wl.KV
+    rows, cols = case.tokens, case.cols
+    base = [to_dev_bf16(wl.draw_kv(case, w)) for w in (0, 1)]
+    xs, ss, qs, ys = [], [], [], []
+    for layer in range(case.layers):
+        for w in (0, 1):
+            x = (base[w].float() * float(2.0 ** (layer / 4 - 2))).to(torch.bfloat16)
+            xs.append(x)
+            ss.append(float(nv.kv_scale(x).item()))  # static calibration, shipped with the model
+            qs.append(torch.empty((rows, cols), dtype=torch.uint8, device="cuda"))
+            ys.append(torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"))
+    del base
+    n = len(xs)
+    quant = lambda i: nv.kv_quantize(xs[i % n], ss[i % n], out=qs[i % n])  # noqa: E731
+    deq = lambda i: nv.kv_dequantize(qs[i % n], ss[i % n], out=ys[i % n])  # noqa: E731
+    for i in range(warmup * n):
+        quant(i)
+        deq(i)
+    torch.cuda.synchronize()
+    q_ms = _time_loop(quant, steps * n)
+    d_ms = _time_loop(deq, steps * n)
+    elems = rows * cols
+    q_gbps = 3.0 * elems / (q_ms * 1e-3) / 1e9
+    d_gbps = 3.0 * elems / (d_ms * 1e-3) / 1e9
+    log(f"[gpu] kv_quantize {q_ms * 1e3:.1f} us/tensor ({q_gbps:.0f} GB/s), "
+        f"kv_dequantize {d_ms * 1e3:.1f} us/tensor ({d_gbps:.0f} GB/s)")
+    # sampled parity: layer 0's K cache, first 2048 tokens, against the oracle from the same input
+    xb = xs[0][:2048].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    parity = bool((qs[0][:2048].cpu().numpy() == oracle.kv_quantize(xb, np.float32(ss[0]))).all())
+    out = {
+        "metric": "FP8 E4M3 KV-cache quantize GB/s (static per-tensor scales), % of HBM roofline",
+        "value": q_gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": (q_ms + d_ms) * n, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, e4m3 out (f32 arithmetic)", "data": "synthetic (seeded normal K/V, hot key channels)",
+        "config": {"workload": case.name, "tensors": n, "rows": rows, "cols": cols},
+        "kv_dequantize_gbps": d_gbps,
+        "roofline": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": q_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "kv_quantize_kernel",
+                     "avg_ms": q_ms, "algorithmic_bytes": 3 * elems},
+        "roofline_dequantize": {"bound": "hbm", "achieved": d_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": d_gbps / PEAK_HBM_GBPS, "kernel": "kv_dequantize_kernel", "avg_ms": d_ms,
+                                "algorithmic_bytes": 3 * elems},
+        "parity_sample": {"layer0_K_first_2048_tokens_bit_exact": parity},
+    }
+    if cpu:
+        rows_cpu = 8192
+        xb = xs[0][:rows_cpu].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.kv_quantize(xb, np.float32(ss[0]))
+        t = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 3.0 * rows_cpu * cols / t / 1e9, "unit": "GB/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"oracle kv_quantize of {rows_cpu} x {cols} (one tensor's first "
+                                         f"{rows_cpu} tokens), {t:.2f}s"}
+    return out
+
+
+def bench_rmsnorm_quantize(steps: int, warmup: int, cpu: bool) -> dict:
+    """One step = RMSNorm of X [32768, 5120] fused with the NVFP4 quantizer of its output (static g,
+    calibrated before timing); also timed: the same two steps as separate kernels (norm writing bf16
+    y, then the quantizer reading it)."""
+    import oracle
+    case = wl.NORM
+    rows, K = case.rows, case.K
+    x_bits = wl.draw_norm_x(case)
+    w_bits = wl.draw_norm_weight(case)
+    x, w = to_dev_bf16(x_bits), to_dev_bf16(w_bits)
+    eps = 1e-6
+    y = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+    codes, scales = nv.alloc_nvfp4(rows, K, "cuda")
+    g0 = 1.0
+    nv.rmsnorm_quantize(x, w, eps, g0, codes, scales, y=y)
+    g = float(nv.global_scale(y).item())  # static calibration of the consuming module
+    fused = lambda i: nv.rmsnorm_quantize(x, w, eps, g, codes, scales)  # noqa: E731
+
+    def unfused(i):
+        nv.rmsnorm_quantize(x, w, eps, g, codes, scales, y=y)
+        nv.quantize(y, g, codes, scales)
+    for i in range(warmup):
+        fused(i)
+        unfused(i)
+    torch.cuda.synchronize()
+    f_ms = _time_loop(fused, steps)
+    u_ms = _time_loop(unfused, steps)
+    alg = rows * K * (2.0 + 0.5625) + 2 * K
+    f_gbps = alg / (f_ms * 1e-3) / 1e9
+    log(f"[gpu] rmsnorm+quantize fused {f_ms:.3f} ms ({f_gbps:.0f} GB/s), as two kernels {u_ms:.3f} ms")
+    yb = oracle.rmsnorm(x_bits[:256], w_bits, np.float32(eps))[0]
+    c_ref, s_ref = oracle.quantize(yb, np.float32(g))
+    parity = bool((codes[:256].cpu().numpy() == c_ref).all() and (scales[:256].cpu().numpy() == s_ref).all())
+    out = {
+        "metric": "RMSNorm + NVFP4 quantize (fused) GB/s, % of HBM roofline",
+        "value": f_gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": f_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, NVFP4 out (f64 row sums, f32 rounding steps)",
+        "data": "synthetic (seeded heavy-tailed activations with outlier channels)",
+        "config": {"workload": case.name, "rows": rows, "K": K},
+        "two_kernel_ms": u_ms, "fused_speedup": u_ms / f_ms,
+        "roofline": {"bound": "hbm", "achieved": f_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": f_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "rmsnorm_quantize_kernel",
+                     "avg_ms": f_ms, "algorithmic_bytes": alg},
+        "parity_sample": {"first_256_rows_bit_exact": parity},
+    }
+    if cpu:
+        rows_cpu = 4096
+        t0 = time.perf_counter()
+        yb = oracle.rmsnorm(x_bits[:rows_cpu], w_bits, np.float32(eps))[0]
+        oracle.quantize(yb, np.float32(g))
+        t = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": (rows_cpu * K * 2.5625) / t / 1e9, "unit": "GB/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"oracle rmsnorm + quantize of the first {rows_cpu} rows, {t:.2f}s"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C5", choices=sorted(wl.ALL))
+    ap.add_argument("--workload", default="C5", choices=sorted(wl.ALL) + list(COMPANIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-quant", type=int, default=32768)
     ap.add_argument("--cpu-rows-gemm", type=int, default=4096)
@@ -245,6 +382,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     nv.lib()  # fail loudly if the HIP library is missing
+    if args.workload in COMPANIONS:
+        fn = {"kv_cache": bench_kv_cache, "rmsnorm_quantize": bench_rmsnorm_quantize}[args.workload]
+        print(json.dumps(fn(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        return 0
     case = wl.ALL[args.workload]
     # a step whose working set fits the 256 MB last-level cache would be served from it: such steps
     # rotate through copies of the weights, 1 GiB in all

@@ -167,8 +167,8 @@ nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int6
  *   q = E4M3_RNE_SAT(RN32(x / s)) per element: round to nearest even, saturating at +-448 (also
  *   for infinities), sign kept (-0.0 and values rounding to zero give 0x80), NaN -> 0x7F.
  *   x_bf16: device bf16 [rows, cols], stride ldx elements, 16-byte aligned, ldx % 8 == 0;
- *   q: device uint8 [rows, cols], stride ldq bytes, 8-byte aligned, ldq % 8 == 0;
- *   s: host float, finite and > 0. cols must be a multiple of 8. rows == 0 or cols == 0: no-op.
+ *   q: device uint8 [rows, cols], stride ldq bytes, 16-byte aligned, ldq % 16 == 0;
+ *   s: host float, finite and > 0. cols must be a multiple of 16. rows == 0 or cols == 0: no-op.
  * Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
  */
 nvfp4_status nvfp4_kv_quantize(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float s,
@@ -177,9 +177,9 @@ nvfp4_status nvfp4_kv_quantize(const void* x_bf16, int64_t rows, int64_t cols, i
 /*
  * nvfp4_kv_dequantize -- FP8 E4M3FN KV-cache dequantization with the same static scale:
  *   y = bf16_RNE(RN32(e4m3(q) * s)); NaN codes (0x7F, 0xFF) give the bf16 NaN 0x7FC0.
- *   q: device uint8 [rows, cols], stride ldq bytes (8-byte aligned, ldq % 8 == 0);
+ *   q: device uint8 [rows, cols], stride ldq bytes (16-byte aligned, ldq % 16 == 0);
  *   y_bf16: device bf16 [rows, cols], stride ldy elements (16-byte aligned, ldy % 8 == 0).
- * cols must be a multiple of 8. Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
+ * cols must be a multiple of 16. Errors: NULL, SHAPE, ALIGN, SCALE, HIP.
  */
 nvfp4_status nvfp4_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, float s,
                                  void* y_bf16, int64_t ldy, void* stream);

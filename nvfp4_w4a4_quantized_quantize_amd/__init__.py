@@ -219,7 +219,7 @@ def kv_quantize(x: torch.Tensor, s: float, out: Optional[torch.Tensor] = None, s
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    _check(lib().nvfp4_kv_quantize(_ptr(x), x.shape[0], x.shape[1], _ld(x, 8), float(s), _ptr(out), _ld(out, 8),
+    _check(lib().nvfp4_kv_quantize(_ptr(x), x.shape[0], x.shape[1], _ld(x, 8), float(s), _ptr(out), _ld(out, 16),
                                    _stream(stream)), "nvfp4_kv_quantize")
     return out
 
@@ -229,7 +229,7 @@ def kv_dequantize(q: torch.Tensor, s: float, out: Optional[torch.Tensor] = None,
     assert q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    _check(lib().nvfp4_kv_dequantize(_ptr(q), q.shape[0], q.shape[1], _ld(q, 8), float(s), _ptr(out), _ld(out, 8),
+    _check(lib().nvfp4_kv_dequantize(_ptr(q), q.shape[0], q.shape[1], _ld(q, 16), float(s), _ptr(out), _ld(out, 8),
                                      _stream(stream)), "nvfp4_kv_dequantize")
     return out
 

@@ -191,19 +191,19 @@ nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int6
 
 namespace {
 
-// An FP8 byte matrix [rows, cols] with stride ldq: 8-byte aligned base and stride.
+// An FP8 byte matrix [rows, cols] with stride ldq: 16-byte aligned base and stride.
 nvfp4_status check_fp8_matrix(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const char* name) {
     if (rows == 0 || cols == 0) return NVFP4_OK;
     if (!q) return fail(NVFP4_ERR_NULL, "%s is NULL", name);
     if (ldq < cols) return fail(NVFP4_ERR_SHAPE, "%s: row stride %lld < cols = %lld", name, (long long)ldq, (long long)cols);
-    if ((reinterpret_cast<uintptr_t>(q) & 7u) != 0 || ldq % 8 != 0)
-        return fail(NVFP4_ERR_ALIGN, "%s: base must be 8-byte aligned and the row stride a multiple of 8", name);
+    if (!aligned16(q) || ldq % 16 != 0)
+        return fail(NVFP4_ERR_ALIGN, "%s: base must be 16-byte aligned and the row stride a multiple of 16", name);
     return NVFP4_OK;
 }
 
 nvfp4_status check_kv_shape(int64_t rows, int64_t cols, float s) {
     if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
-    if (cols % 8 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 8", (long long)cols);
+    if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
     if (!good_scale(s)) return fail(NVFP4_ERR_SCALE, "KV scale s = %g must be finite and > 0", (double)s);
     return NVFP4_OK;
 }

@@ -71,8 +71,15 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    // non-negative floats order like their bit patterns, so an integer max is exact
-    if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(acc, __float_as_uint(m));
+    // one atomic per workgroup: same-address atomics serialize in L2
+    __shared__ float wave_max[4];
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+        // non-negative floats order like their bit patterns, so an integer max is exact
+        if (m > 0.0f) atomicMax(acc, __float_as_uint(m));
+    }
 }
 
 __global__ void finish_scale_kernel(float* g_out, float divisor) {
@@ -89,7 +96,7 @@ hipError_t launch_amax_scale(const uint16_t* x, int64_t rows, int64_t K, int64_t
     uint32_t* acc = reinterpret_cast<uint32_t*>(g_out);
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, acc);
     if (rows > 0 && K > 0) {
-        const int64_t grid = rows < 8192 ? rows : 8192;
+        const int64_t grid = rows < 1024 ? rows : 1024;
         hipLaunchKernelGGL(amax_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, rows, K, ldx, acc);
     }
     hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(64), 0, stream, g_out, divisor);

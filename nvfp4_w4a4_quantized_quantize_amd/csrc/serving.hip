@@ -34,31 +34,30 @@ __device__ __forceinline__ uint32_t e4m3_signed(float q, float xsign) {
     return (__float_as_uint(xsign) >> 24 & 0x80u) | mag;
 }
 
-// ---- FP8 KV codec: one thread = 8 consecutive elements ----------------------------------------
+// ---- FP8 KV codec: one thread = 16 consecutive elements (32 bytes of bf16, 16 bytes of FP8) ----
+__device__ __forceinline__ uint32_t kv_pair(uint32_t w, float s, float y, bool s_ok) {
+    const float f0 = bf16_lo(w), f1 = bf16_hi(w);
+    const uint32_t b0 = e4m3_signed(quotient_rn(fabsf(f0), s, y, s_ok), f0);
+    const uint32_t b1 = e4m3_signed(quotient_rn(fabsf(f1), s, y, s_ok), f1);
+    return b0 | (b1 << 8);
+}
+
 __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                           uint8_t* __restrict__ q, int64_t ldq, float s,
                                                           uint32_t units, uint32_t blocks_per_row) {
     const uint32_t row = blockIdx.x / blocks_per_row;
     const uint32_t u = (blockIdx.x - row * blocks_per_row) * 256u + threadIdx.x;
     if (u >= units) return;
-    const qu32x4 p = __builtin_nontemporal_load(reinterpret_cast<const qu32x4*>(x + (int64_t)row * ldx + 8u * u));
+    const qu32x4* src = reinterpret_cast<const qu32x4*>(x + (int64_t)row * ldx + 16u * u);
+    const qu32x4 p0 = __builtin_nontemporal_load(src), p1 = __builtin_nontemporal_load(src + 1);
     const float y = __builtin_amdgcn_rcpf(s);
     const bool s_ok = s >= 0x1p-100f && s <= 0x1p100f;
-    uint32_t out[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t w = p[2 * h + i];
-            const float f0 = bf16_lo(w), f1 = bf16_hi(w);
-            const uint32_t b0 = e4m3_signed(quotient_rn(fabsf(f0), s, y, s_ok), f0);
-            const uint32_t b1 = e4m3_signed(quotient_rn(fabsf(f1), s, y, s_ok), f1);
-            word |= (b0 | (b1 << 8)) << (16 * i);
-        }
-        out[h] = word;
-    }
-    __builtin_nontemporal_store(qu32x2{out[0], out[1]}, reinterpret_cast<qu32x2*>(q + (int64_t)row * ldq + 8u * u));
+    qu32x4 o;
+    o[0] = kv_pair(p0[0], s, y, s_ok) | (kv_pair(p0[1], s, y, s_ok) << 16);
+    o[1] = kv_pair(p0[2], s, y, s_ok) | (kv_pair(p0[3], s, y, s_ok) << 16);
+    o[2] = kv_pair(p1[0], s, y, s_ok) | (kv_pair(p1[1], s, y, s_ok) << 16);
+    o[3] = kv_pair(p1[2], s, y, s_ok) | (kv_pair(p1[3], s, y, s_ok) << 16);
+    __builtin_nontemporal_store(o, reinterpret_cast<qu32x4*>(q + (int64_t)row * ldq + 16u * u));
 }
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
@@ -72,19 +71,21 @@ __global__ __launch_bounds__(256) void kv_dequantize_kernel(const uint8_t* __res
     const uint32_t row = blockIdx.x / blocks_per_row;
     const uint32_t u = (blockIdx.x - row * blocks_per_row) * 256u + threadIdx.x;
     if (u >= units) return;
-    const qu32x2 p = __builtin_nontemporal_load(reinterpret_cast<const qu32x2*>(q + (int64_t)row * ldq + 8u * u));
-    qu32x4 o;
+    const qu32x4 p = __builtin_nontemporal_load(reinterpret_cast<const qu32x4*>(q + (int64_t)row * ldq + 16u * u));
+    qu32x4 o[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 4; ++h) {
         const int w = (int)p[h];
         const float v0 = __builtin_amdgcn_cvt_f32_fp8(w, 0) * s;
         const float v1 = __builtin_amdgcn_cvt_f32_fp8(w, 1) * s;
         const float v2 = __builtin_amdgcn_cvt_f32_fp8(w, 2) * s;
         const float v3 = __builtin_amdgcn_cvt_f32_fp8(w, 3) * s;
-        o[2 * h] = bf16_bits_rne(v0) | (bf16_bits_rne(v1) << 16);
-        o[2 * h + 1] = bf16_bits_rne(v2) | (bf16_bits_rne(v3) << 16);
+        o[h >> 1][2 * (h & 1)] = bf16_bits_rne(v0) | (bf16_bits_rne(v1) << 16);
+        o[h >> 1][2 * (h & 1) + 1] = bf16_bits_rne(v2) | (bf16_bits_rne(v3) << 16);
     }
-    __builtin_nontemporal_store(o, reinterpret_cast<qu32x4*>(y + (int64_t)row * ldy + 8u * u));
+    qu32x4* dst = reinterpret_cast<qu32x4*>(y + (int64_t)row * ldy + 16u * u);
+    __builtin_nontemporal_store(o[0], dst);
+    __builtin_nontemporal_store(o[1], dst + 1);
 }
 
 // ---- fold-in repair: one thread = one scale byte, in place -------------------------------------
@@ -104,7 +105,59 @@ __global__ __launch_bounds__(256) void fold_scales_kernel(uint8_t* __restrict__ 
 //   ms = sum(x^2) / K in double; r = RN32(1 / sqrt(ms + eps)) (double, then one rounding);
 //   y1 = bf16_RNE(RN32(x r)); y = bf16_RNE(y1 w) (the product of two bf16 values is exact in FP32);
 //   then y is encoded as NVFP4 with the static global scale g.
-// The row is read twice: the second pass finds it in L2, so HBM sees it once.
+// Lane l owns the 16-element blocks l, l + 64, ... of its row. With NBL > 0 (rows of at most
+// 64 * NBL blocks) the row stays in registers between the sum and the encoding, so it is read
+// once; NBL == 0 handles any K with a second pass over the row, which finds it in L2.
+__device__ __forceinline__ double sum_squares16(const qu32x4& p0, const qu32x4& p1) {
+    const uint32_t wv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double lo = bf16_lo(wv[i]), hi = bf16_hi(wv[i]);
+        ss += lo * lo;
+        ss += hi * hi;
+    }
+    return ss;
+}
+
+__device__ __forceinline__ void norm_encode_block(const qu32x4& p0, const qu32x4& p1, const qu32x4& w0,
+                                                  const qu32x4& w1, int64_t b, float r, float g,
+                                                  uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
+                                                  uint16_t* __restrict__ y_row) {
+    const uint32_t xv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float y1lo = (float)(__bf16)(bf16_lo(xv[i]) * r);
+        const float y1hi = (float)(__bf16)(bf16_hi(xv[i]) * r);
+        f[2 * i] = (float)(__bf16)(y1lo * bf16_lo(wv[i]));
+        f[2 * i + 1] = (float)(__bf16)(y1hi * bf16_hi(wv[i]));
+    }
+    const Block16 q = encode_block16(f, g);
+    __builtin_nontemporal_store(qu32x2{q.c0, q.c1}, reinterpret_cast<qu32x2*>(codes_row + 8 * b));
+    scales_row[b] = (uint8_t)q.sb;
+    if (y_row) {
+        qu32x4 o0, o1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o0[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+            o1[i] = (__float_as_uint(f[8 + 2 * i]) >> 16) | (__float_as_uint(f[8 + 2 * i + 1]) & 0xffff0000u);
+        }
+        qu32x4* dst = reinterpret_cast<qu32x4*>(y_row + 16 * b);
+        dst[0] = o0;
+        dst[1] = o1;
+    }
+}
+
+__device__ __forceinline__ float row_rscale(double ss, int64_t K, float eps) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const double ms = __ddiv_rn(ss, (double)K);
+    return (float)__ddiv_rn(1.0, __dsqrt_rn(ms + (double)eps));
+}
+
+template <int NBL>
 __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* __restrict__ w, float eps,
     float g, uint8_t* __restrict__ codes, int64_t ldc, uint8_t* __restrict__ scales, int64_t lds,
@@ -114,51 +167,53 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     if (row >= rows) return;
     const int64_t nb = K / 16;
     const uint16_t* xr = x + row * ldx;
+    uint8_t* codes_row = codes + row * ldc;
+    uint8_t* scales_row = scales + row * lds;
+    uint16_t* y_row = y_out ? y_out + row * ldy : nullptr;
 
-    double ss = 0.0;
-    for (int64_t b = lane; b < nb; b += 64) {
-        const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
-        const qu32x4 p0 = src[0], p1 = src[1];
-        const uint32_t wv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    if constexpr (NBL > 0) {
+        // the row and the matching norm weights are loaded together, so the weights' latency hides
+        // behind the row's and the reduction
+        qu32x4 p[NBL][2], wt[NBL][2];
+        double ss = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const double lo = bf16_lo(wv[i]), hi = bf16_hi(wv[i]);
-            ss += lo * lo;
-            ss += hi * hi;
-        }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    const double ms = __ddiv_rn(ss, (double)K);
-    const float r = (float)__ddiv_rn(1.0, __dsqrt_rn(ms + (double)eps));
-
-    for (int64_t b = lane; b < nb; b += 64) {
-        const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
-        const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
-        const qu32x4 p0 = src[0], p1 = src[1], w0 = wsrc[0], w1 = wsrc[1];
-        const uint32_t xv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        float f[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y1lo = (float)(__bf16)(bf16_lo(xv[i]) * r);
-            const float y1hi = (float)(__bf16)(bf16_hi(xv[i]) * r);
-            f[2 * i] = (float)(__bf16)(y1lo * bf16_lo(wv[i]));
-            f[2 * i + 1] = (float)(__bf16)(y1hi * bf16_hi(wv[i]));
-        }
-        const Block16 q = encode_block16(f, g);
-        *reinterpret_cast<qu32x2*>(codes + row * ldc + 8 * b) = qu32x2{q.c0, q.c1};
-        scales[row * lds + b] = (uint8_t)q.sb;
-        if (y_out) {
-            qu32x4 o0, o1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o0[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
-                o1[i] = (__float_as_uint(f[8 + 2 * i]) >> 16) | (__float_as_uint(f[8 + 2 * i + 1]) & 0xffff0000u);
+        for (int j = 0; j < NBL; ++j) {
+            const int64_t b = lane + 64 * j;
+            if (b < nb) {
+                const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
+                p[j][0] = __builtin_nontemporal_load(src);
+                p[j][1] = __builtin_nontemporal_load(src + 1);
             }
-            qu32x4* dst = reinterpret_cast<qu32x4*>(y_out + row * ldy + 16 * b);
-            dst[0] = o0;
-            dst[1] = o1;
+        }
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int64_t b = lane + 64 * j;
+            if (b < nb) {
+                const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
+                wt[j][0] = wsrc[0];
+                wt[j][1] = wsrc[1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NBL; ++j)
+            if (lane + 64 * j < nb) ss += sum_squares16(p[j][0], p[j][1]);
+        const float r = row_rscale(ss, K, eps);
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int64_t b = lane + 64 * j;
+            if (b < nb) norm_encode_block(p[j][0], p[j][1], wt[j][0], wt[j][1], b, r, g, codes_row, scales_row, y_row);
+        }
+    } else {
+        double ss = 0.0;
+        for (int64_t b = lane; b < nb; b += 64) {
+            const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
+            ss += sum_squares16(src[0], src[1]);
+        }
+        const float r = row_rscale(ss, K, eps);
+        for (int64_t b = lane; b < nb; b += 64) {
+            const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
+            const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
+            norm_encode_block(src[0], src[1], wsrc[0], wsrc[1], b, r, g, codes_row, scales_row, y_row);
         }
     }
 }
@@ -182,8 +237,8 @@ hipError_t launch_kv_quantize(const uint16_t* x, int64_t rows, int64_t cols, int
         rows = 1;
     }
     uint32_t bpr, grid;
-    if (!row_grid(rows, cols / 8, &bpr, &grid)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kv_quantize_kernel, dim3(grid), dim3(256), 0, stream, x, ldx, q, ldq, s, (uint32_t)(cols / 8), bpr);
+    if (!row_grid(rows, cols / 16, &bpr, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kv_quantize_kernel, dim3(grid), dim3(256), 0, stream, x, ldx, q, ldq, s, (uint32_t)(cols / 16), bpr);
     return hipGetLastError();
 }
 
@@ -195,8 +250,8 @@ hipError_t launch_kv_dequantize(const uint8_t* q, int64_t rows, int64_t cols, in
         rows = 1;
     }
     uint32_t bpr, grid;
-    if (!row_grid(rows, cols / 8, &bpr, &grid)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kv_dequantize_kernel, dim3(grid), dim3(256), 0, stream, q, ldq, y, ldy, s, (uint32_t)(cols / 8), bpr);
+    if (!row_grid(rows, cols / 16, &bpr, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kv_dequantize_kernel, dim3(grid), dim3(256), 0, stream, q, ldq, y, ldy, s, (uint32_t)(cols / 16), bpr);
     return hipGetLastError();
 }
 
@@ -219,7 +274,13 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t K, i
     if (rows == 0 || K == 0) return hipSuccess;
     const int64_t grid = (rows + 3) / 4;
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(rmsnorm_quantize_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, rows, K, ldx, w, eps,
+    typedef void (*fn_t)(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, float, float, uint8_t*, int64_t,
+                         uint8_t*, int64_t, uint16_t*, int64_t);
+    static const fn_t by_nbl[9] = {rmsnorm_quantize_kernel<0>, rmsnorm_quantize_kernel<1>, rmsnorm_quantize_kernel<2>,
+                                   rmsnorm_quantize_kernel<3>, rmsnorm_quantize_kernel<4>, rmsnorm_quantize_kernel<5>,
+                                   rmsnorm_quantize_kernel<6>, rmsnorm_quantize_kernel<7>, rmsnorm_quantize_kernel<8>};
+    const int64_t nbl = (K / 16 + 63) / 64;  // blocks per lane
+    hipLaunchKernelGGL(by_nbl[nbl <= 8 ? nbl : 0], dim3((uint32_t)grid), dim3(256), 0, stream, x, rows, K, ldx, w, eps,
                        g, codes, ldc, scales, lds, y, ldy);
     return hipGetLastError();
 }

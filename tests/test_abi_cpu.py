@@ -125,8 +125,8 @@ def kvq(L, x=A16, rows=4, cols=64, ldx=64, s=0.5, q=A16, ldq=64):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), 1), (dict(q=None), 1),
-    (dict(cols=60, ldx=64, ldq=64), 2), (dict(rows=-1), 2), (dict(ldx=56), 2), (dict(ldq=32), 2),
-    (dict(x=A16 + 8), 3), (dict(ldx=68), 3), (dict(q=A16 + 4), 3), (dict(ldq=68), 3),
+    (dict(cols=56, ldx=64, ldq=64), 2), (dict(rows=-1), 2), (dict(ldx=56), 2), (dict(ldq=32), 2),
+    (dict(x=A16 + 8), 3), (dict(ldx=68), 3), (dict(q=A16 + 8), 3), (dict(ldq=72), 3),
     (dict(s=0.0), 5), (dict(s=float("nan")), 5), (dict(s=float("inf")), 5),
 ])
 def test_kv_quantize_rejects(L, kw, status):
@@ -135,8 +135,8 @@ def test_kv_quantize_rejects(L, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(y=None), 1), (dict(cols=12, ldq=16, ldy=16), 2), (dict(y=A16 + 2), 3),
-    (dict(q=A16 + 1), 3), (dict(s=-2.0), 5),
+    (dict(q=None), 1), (dict(y=None), 1), (dict(cols=24, ldq=32, ldy=32), 2), (dict(y=A16 + 2), 3),
+    (dict(q=A16 + 8), 3), (dict(s=-2.0), 5),
 ])
 def test_kv_dequantize_rejects(L, kw, status):
     a = dict(q=A16, rows=4, cols=64, ldq=64, s=0.5, y=A16, ldy=64)

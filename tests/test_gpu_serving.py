@@ -40,8 +40,8 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ FP8 KV codec
-@pytest.mark.parametrize("rows,cols,strided", [(1, 8, False), (3, 136, True), (257, 1024, False),
-                                               (64, 128, True), (4096, 1024, False)])
+@pytest.mark.parametrize("rows,cols,strided", [(1, 16, False), (3, 144, True), (257, 1024, False),
+                                               (64, 128, True), (4096, 1024, False), (1, 48, False)])
 @pytest.mark.parametrize("s", [0.0123, 2.0 ** -110, 3.0e30])
 def test_kv_quantize_bit_exact(rows, cols, strided, s):
     rng = np.random.default_rng(rows * 31 + cols)
@@ -65,9 +65,9 @@ def test_kv_dequantize_all_codes(s):
 
 def test_kv_dequantize_strided_and_scale():
     rng = np.random.default_rng(11)
-    rows, cols = 37, 200
+    rows, cols = 37, 208
     q = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
-    qbuf = torch.zeros((rows, 208), dtype=torch.uint8, device=DEV)
+    qbuf = torch.zeros((rows, 224), dtype=torch.uint8, device=DEV)
     qbuf[:, :cols] = dev_u8(q)
     ybuf = torch.full((rows, 216), float("nan"), dtype=torch.bfloat16, device=DEV)
     nv.kv_dequantize(qbuf[:, :cols], 0.07, out=ybuf[:, :cols])

@@ -188,3 +188,58 @@ def draw_gate_params(case: GemmCase, seg_index: int, seed: int = 0, n: int | Non
     a_log = (g.standard_normal(n, dtype=np.float32) * np.float32(0.5)).astype(np.float32)
     dt_bias = (g.standard_normal(n, dtype=np.float32) * np.float32(0.5)).astype(np.float32)
     return a_log, dt_bias
+
+
+# ------------------------------------------------------------------ serving-path companions
+@dataclasses.dataclass(frozen=True)
+class KvCase:
+    """K and V caches of the attention layers for one prefill: [tokens, kv_heads * head_dim] each.
+    The pages give 16 softmax-attention layers out of 64 and 32 shipped KV scales (Japanese article,
+    "Is FP8 enough for the KV cache?"); 8 KV heads of 128 dimensions is this recipe's choice (the
+    pages do not give the attention geometry). Keys get a few hot channels, values none."""
+    name: str
+    cfg_id: int
+    tokens: int
+    kv_heads: int
+    head_dim: int
+    layers: int
+
+    @property
+    def cols(self) -> int:
+        return self.kv_heads * self.head_dim
+
+
+KV = KvCase("kv_cache_16x2x32768x1024", 40, 32768, 8, 128, 16)
+KV_DISTS = (Dist("normal", 1.0, n_outliers=8, outlier_mult=10.0), Dist("normal", 1.0))
+
+
+def draw_kv(case: KvCase, which: int, seed: int = 0, row_begin: int = 0, row_end: int | None = None,
+            tokens: int | None = None) -> np.ndarray:
+    """bf16 bits [tokens, cols] of the K (which = 0) or V (which = 1) cache of one layer."""
+    tokens = case.tokens if tokens is None else tokens
+    return draw_matrix(seed, case.cfg_id, which, tokens, case.cols, KV_DISTS[which], row_begin, row_end)
+
+
+@dataclasses.dataclass(frozen=True)
+class NormCase:
+    """RMSNorm ahead of a quantized projection: X [rows, K] with the heavy-tailed activation recipe
+    and a bf16 norm weight drawn uniformly from [0.5, 1.5]."""
+    name: str
+    cfg_id: int
+    rows: int
+    K: int
+    x_dist: Dist
+
+
+NORM = NormCase("rmsnorm_quantize_32768x5120", 50, 32768, HIDDEN, heavy(HIDDEN))
+
+
+def draw_norm_x(case: NormCase, seed: int = 0, row_begin: int = 0, row_end: int | None = None,
+                rows: int | None = None) -> np.ndarray:
+    rows = case.rows if rows is None else rows
+    return draw_matrix(seed, case.cfg_id, X_TENSOR, rows, case.K, case.x_dist, row_begin, row_end)
+
+
+def draw_norm_weight(case: NormCase, seed: int = 0) -> np.ndarray:
+    g = _rng(seed, case.cfg_id, GATE_TENSOR, 0)
+    return f32_to_bf16_bits(g.uniform(0.5, 1.5, case.K).astype(np.float32))
