@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_fold_scales.argtypes = [P, i64, i64, i64, f32]
         L.oracle_rmsnorm.restype = None
         L.oracle_rmsnorm.argtypes = [P, i64, i64, i64, P, f32, P, i64, P]
+        L.oracle_gdn_recurrence.restype = None
+        L.oracle_gdn_recurrence.argtypes = [P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, i64, i64, i64, i64, P, P]
+        L.oracle_gdn_recurrence_f32.restype = None
+        L.oracle_gdn_recurrence_f32.argtypes = [P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, i64, i64, i64, i64,
+                                                P, P]
         _lib = L
     return _lib
 
@@ -279,3 +284,29 @@ def rmsnorm(x_bf16: np.ndarray, w_bf16: np.ndarray, eps) -> tuple[np.ndarray, np
     r = np.empty(rows, np.float32)
     lib().oracle_rmsnorm(_ptr(x), rows, K, K, _ptr(w), float(np.float32(eps)), _ptr(y), K, _ptr(r))
     return y, r
+
+
+def _gdn_args(q, k, v, alpha, beta, B, T):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    assert q.shape[0] == k.shape[0] == v.shape[0] == alpha.shape[0] == beta.shape[0] == B * T
+    return q, k, v, alpha, beta
+
+
+def gdn_recurrence(q, k, v, alpha, beta, B: int, T: int, D: int = 128, S0=None, f32: bool = False):
+    """The Gated DeltaNet recurrence: q, k bf16 bits [B*T, Hk*D]; v bf16 bits [B*T, Hv*D]; alpha, beta
+    float32 [B*T, Hv]; S0 [B, Hv, D, D] or None. Returns (o [B*T, Hv*D], S_T [B, Hv, D, D]) in double
+    (float32 with f32=True: the float32 twin, for sizing FP32 rounding error)."""
+    q, k, v, alpha, beta = _gdn_args(q, k, v, alpha, beta, B, T)
+    Hk, Hv = q.shape[1] // D, v.shape[1] // D
+    dt = np.float32 if f32 else np.float64
+    o = np.empty((B * T, Hv * D), dt)
+    S = np.empty((B, Hv, D, D), dt)
+    s0 = None if S0 is None else np.ascontiguousarray(S0, dtype=dt)
+    fn = lib().oracle_gdn_recurrence_f32 if f32 else lib().oracle_gdn_recurrence
+    fn(_ptr(q), q.shape[1], _ptr(k), k.shape[1], _ptr(v), v.shape[1], _ptr(alpha), Hv, _ptr(beta), Hv,
+       None if s0 is None else _ptr(s0), B, T, Hv, Hk, D, _ptr(o), _ptr(S))
+    return o, S

@@ -23,7 +23,8 @@
  *    The 'ship KV scales' recipe"; the fold-in repair of the fused-module scale mismatch (common global
  *    scale, ratio folded into the block scales, re-rounding error at most 6.2%) -- Japanese article,
  *    "Trap 1"; the BF16 normalization layers ahead of the quantized projections -- Japanese article,
- *    "Minima, quantized 'all 4-bit': the experiment design".
+ *    "Minima, quantized 'all 4-bit': the experiment design"; the Gated DeltaNet delta-rule recurrence
+ *    that consumes the gates -- Japanese article, "How Gated DeltaNet works".
  *
  * Readings where the pages are silent:
  *  - every FP32 step is one IEEE binary32 operation rounded to nearest-even, in the order
@@ -390,6 +391,90 @@ void oracle_rmsnorm(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, con
             y[i * ldy + k] = bf16_from_float(y1 * bf16_to_float(w[k]));
         }
     }
+}
+
+/* Gated DeltaNet recurrence fed by the gates (Japanese article, "How Gated DeltaNet works"): per
+ * sequence b and value head h, with key head hk = h / (Hv / Hk) and state S [D (key), D (value)],
+ *   S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T,     o_t = S_t^T q_t,
+ * exactly the pages' update (its erase term carries no alpha); the readout o_t = S_t^T q_t is the
+ * usual linear-attention readout (the pages do not write it). Rows are tokens, row r = b * T + t;
+ * q, k: bf16 [B*T, Hk*D] (strides ldq, ldk); v: bf16 [B*T, Hv*D] (ldv); alpha, beta: float
+ * [B*T, Hv] (lda, ldb); S0: double [B, Hv, D, D] (NULL = zeros); outputs o: double [B*T, Hv*D]
+ * (dense) and S_T: double [B, Hv, D, D]. Everything in double. */
+void oracle_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
+                           int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
+                           const double* S0, int64_t B, int64_t T, int64_t Hv, int64_t Hk, int64_t D, double* o,
+                           double* S_out) {
+    const int64_t group = Hv / Hk;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hv; ++h) {
+            const int64_t hk = h / group;
+            double* S = S_out + (b * Hv + h) * D * D;
+            for (int64_t i = 0; i < D * D; ++i) S[i] = S0 ? S0[(b * Hv + h) * D * D + i] : 0.0;
+            double* kt = (double*)malloc(sizeof(double) * (size_t)D);
+            double* qt = (double*)malloc(sizeof(double) * (size_t)D);
+            double* u = (double*)malloc(sizeof(double) * (size_t)D);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t r = b * T + t;
+                for (int64_t i = 0; i < D; ++i) {
+                    kt[i] = bf16_to_float(k[r * ldk + hk * D + i]);
+                    qt[i] = bf16_to_float(q[r * ldq + hk * D + i]);
+                }
+                const double a = alpha[r * lda + h], be = beta[r * ldb + h];
+                for (int64_t j = 0; j < D; ++j) { /* u = v - S^T k, with the old S */
+                    double sk = 0.0;
+                    for (int64_t i = 0; i < D; ++i) sk += S[i * D + j] * kt[i];
+                    u[j] = (double)bf16_to_float(v[r * ldv + h * D + j]) - sk;
+                }
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] = a * S[i * D + j] + be * kt[i] * u[j];
+                for (int64_t j = 0; j < D; ++j) {
+                    double oq = 0.0;
+                    for (int64_t i = 0; i < D; ++i) oq += S[i * D + j] * qt[i];
+                    o[r * Hv * D + h * D + j] = oq;
+                }
+            }
+            free(kt);
+            free(qt);
+            free(u);
+        }
+}
+
+/* The same recurrence in binary32 with the natural order (sequential sums), used only to size the
+ * rounding error of an FP32 implementation on a given input. */
+void oracle_gdn_recurrence_f32(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
+                               int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
+                               const float* S0, int64_t B, int64_t T, int64_t Hv, int64_t Hk, int64_t D, float* o,
+                               float* S_out) {
+    const int64_t group = Hv / Hk;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hv; ++h) {
+            const int64_t hk = h / group;
+            float* S = S_out + (b * Hv + h) * D * D;
+            for (int64_t i = 0; i < D * D; ++i) S[i] = S0 ? S0[(b * Hv + h) * D * D + i] : 0.0f;
+            float* u = (float*)malloc(sizeof(float) * (size_t)D);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t r = b * T + t;
+                const float a = alpha[r * lda + h], be = beta[r * ldb + h];
+                for (int64_t j = 0; j < D; ++j) {
+                    float sk = 0.0f;
+                    for (int64_t i = 0; i < D; ++i) sk += S[i * D + j] * bf16_to_float(k[r * ldk + hk * D + i]);
+                    u[j] = bf16_to_float(v[r * ldv + h * D + j]) - sk;
+                }
+                for (int64_t i = 0; i < D; ++i) {
+                    const float ki = bf16_to_float(k[r * ldk + hk * D + i]);
+                    for (int64_t j = 0; j < D; ++j) S[i * D + j] = a * S[i * D + j] + be * ki * u[j];
+                }
+                for (int64_t j = 0; j < D; ++j) {
+                    float oq = 0.0f;
+                    for (int64_t i = 0; i < D; ++i) oq += S[i * D + j] * bf16_to_float(q[r * ldq + hk * D + i]);
+                    o[r * Hv * D + h * D + j] = oq;
+                }
+            }
+            free(u);
+        }
 }
 
 /* Number of threads the OpenMP row loops use (1 without OpenMP). */

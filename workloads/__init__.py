@@ -243,3 +243,44 @@ def draw_norm_x(case: NormCase, seed: int = 0, row_begin: int = 0, row_end: int 
 def draw_norm_weight(case: NormCase, seed: int = 0) -> np.ndarray:
     g = _rng(seed, case.cfg_id, GATE_TENSOR, 0)
     return f32_to_bf16_bits(g.uniform(0.5, 1.5, case.K).astype(np.float32))
+
+
+@dataclasses.dataclass(frozen=True)
+class GdnCase:
+    """Inputs of the Gated DeltaNet recurrence after the fused in_proj GEMM: B sequences of T tokens,
+    Hv value heads and Hk key heads of D dimensions (the in_proj widths: q/k 2048 = 16 x 128, v 4096
+    = 32 x 128, gates 32). q and k rows are unit-norm per head (as after the model's own
+    normalization, which the pages do not describe), v ~ N(0, 1); the decay alpha is 1 - 10^u with
+    u drawn per head in [-5, -0.5] plus a per-token jitter of +-0.25 (decay horizons from a few
+    tokens to about 10^5, covering the pages' 44K-62K), and the write strength beta ~ U(0.05, 1)."""
+    name: str
+    cfg_id: int
+    B: int
+    T: int
+    Hv: int = 32
+    Hk: int = 16
+    D: int = 128
+
+
+GDN_PREFILL = GdnCase("gdn_recurrence_1x32768", 60, 1, 32768)
+GDN_DECODE = GdnCase("gdn_decode_64x1", 61, 64, 1)
+
+
+def draw_gdn(case: GdnCase, seed: int = 0, T: int | None = None, B: int | None = None):
+    """(q, k, v) bf16 bits and (alpha, beta) float32, rows ordered [b][t]."""
+    T = case.T if T is None else T
+    B = case.B if B is None else B
+    g = _rng(seed, case.cfg_id, 7, B, T)
+    rows = B * T
+
+    def unit_rows(n_heads):
+        x = g.standard_normal((rows, n_heads, case.D), dtype=np.float32)
+        x /= np.linalg.norm(x, axis=2, keepdims=True).astype(np.float32)
+        return f32_to_bf16_bits(x.reshape(rows, n_heads * case.D))
+
+    q, k = unit_rows(case.Hk), unit_rows(case.Hk)
+    v = f32_to_bf16_bits(g.standard_normal((rows, case.Hv * case.D), dtype=np.float32))
+    u = g.uniform(-5.0, -0.5, case.Hv)[None, :] + g.uniform(-0.25, 0.25, (rows, case.Hv))
+    alpha = (1.0 - 10.0 ** u).astype(np.float32)
+    beta = g.uniform(0.05, 1.0, (rows, case.Hv)).astype(np.float32)
+    return q, k, v, alpha, beta
