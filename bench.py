@@ -224,7 +224,8 @@ def run_cpu_baseline(step: Step, rows_quant: int, rows_gemm: int) -> dict:
 
 
 # ----------------------------------------------------------------------- serving-path companions
-COMPANIONS = ("kv_cache", "rmsnorm_quantize")
+COMPANIONS = ("kv_cache", "rmsnorm_quantize", "gdn_prefill", "gdn_decode")
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X FP32 vector peak (256 CUs, 2.4 GHz)
 
 
 def _time_loop(fn, n: int) -> float:
@@ -360,6 +361,69 @@ def bench_rmsnorm_quantize(steps: int, warmup: int, cpu: bool) -> dict:
     return out
 
 
+def bench_gdn(case, steps: int, warmup: int, cpu: bool) -> dict:
+    """The Gated DeltaNet recurrence over one batch: gdn_prefill = one sequence of 32768 tokens, all 32
+    value heads (FP32 arithmetic, 6 D^2 flops per token and head: S^T k, the update, S^T q);
+    gdn_decode = one token for each of 64 sequences, which streams every head's 64 KB state in and out."""
+    import oracle
+    B, T, Hv, D = case.B, case.T, case.Hv, case.D
+    q, k, v, a, b = wl.draw_gdn(case)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    ad, bd = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    # decode: rotate 4 state buffers (4 x 268 MB) so each step streams its state from HBM
+    copies = 1 if T > 1 else 4
+    states = [torch.zeros((B, Hv, D, D), dtype=torch.float32, device="cuda") for _ in range(copies)]
+    o = torch.empty((B * T, Hv * D), dtype=torch.float32, device="cuda")
+    run = lambda i: nv.gdn_recurrence(qd, kd, vd, ad, bd, states[i % copies], B, T, o=o)  # noqa: E731
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ms = _time_loop(run, steps)
+    flops = 6.0 * D * D * Hv * B * T
+    tflops = flops / (ms * 1e-3) / 1e12
+    state_bytes = 2.0 * B * Hv * D * D * 4
+    in_bytes = B * T * (2 * 16 * D * 2 + Hv * D * 2 + 2 * Hv * 4) + B * T * Hv * D * 4
+    gbps = (state_bytes + in_bytes) / (ms * 1e-3) / 1e9
+    log(f"[gpu] gdn {case.name}: {ms:.3f} ms per call, {B * T / (ms * 1e-3) / 1e6:.2f} M tokens/s, "
+        f"{tflops:.2f} TFLOP/s, {gbps:.0f} GB/s")
+    # sampled parity: the first 64 tokens of sequence 0, all heads, from a zero state
+    n = min(T, 64)
+    st = torch.zeros((1, Hv, D, D), dtype=torch.float32, device="cuda")
+    og = nv.gdn_recurrence(qd[:n], kd[:n], vd[:n], ad[:n], bd[:n], st, 1, n).cpu().numpy().astype(np.float64)
+    o64, _ = oracle.gdn_recurrence(q[:n], k[:n], v[:n], a[:n], b[:n], 1, n)
+    o32, _ = oracle.gdn_recurrence(q[:n], k[:n], v[:n], a[:n], b[:n], 1, n, f32=True)
+    parity = bool(np.abs(og - o64).max() <= 8 * np.abs(o32 - o64).max() + 2.0 ** -22 * np.abs(o64).max())
+    if T > 1:
+        roof = {"bound": "alu", "achieved": tflops, "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_F32_VALU_TFLOPS, "traffic": None, "kernel": "gdn_recurrence_kernel",
+                "avg_ms": ms, "algorithmic_flop": flops}
+        metric, value, unit = "Gated DeltaNet recurrence tokens/s (FP32, 32 heads)", B * T / (ms * 1e-3), "tokens/s"
+    else:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                "traffic": None, "kernel": "gdn_recurrence_kernel", "avg_ms": ms,
+                "algorithmic_bytes": state_bytes + in_bytes}
+        metric, value, unit = "Gated DeltaNet decode step GB/s (state in + out), % of HBM roofline", gbps, "GB/s"
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded unit-norm q/k, normal v, decays over horizons 3..1e5 tokens)",
+           "config": {"workload": case.name, "B": B, "T": T, "Hv": Hv, "Hk": case.Hk, "D": D},
+           "tflops": tflops, "gbps": gbps, "roofline": roof,
+           "parity_sample": {"first_64_tokens_within_fp32_bound": parity}}
+    if cpu:
+        Tc = min(T, 512)
+        t0 = time.perf_counter()
+        oracle.gdn_recurrence(q[:Tc * B], k[:Tc * B], v[:Tc * B], a[:Tc * B], b[:Tc * B], B, Tc) if T == 1 else \
+            oracle.gdn_recurrence(q[:Tc], k[:Tc], v[:Tc], a[:Tc], b[:Tc], 1, Tc)
+        t = time.perf_counter() - t0
+        toks = Tc * B if T == 1 else Tc
+        cpu_v = toks / t if T > 1 else 6.0 * D * D * Hv * toks / t / 1e12
+        out["cpu_baseline"] = {"value": cpu_v if T > 1 else (state_bytes / B * toks) / t / 1e9,
+                               "unit": "tokens/s" if T > 1 else "GB/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"oracle recurrence (double) over {toks} tokens x {Hv} heads, {t:.2f}s"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,7 +447,9 @@ def main() -> int:
         return 2
     nv.lib()  # fail loudly if the HIP library is missing
     if args.workload in COMPANIONS:
-        fn = {"kv_cache": bench_kv_cache, "rmsnorm_quantize": bench_rmsnorm_quantize}[args.workload]
+        fn = {"kv_cache": bench_kv_cache, "rmsnorm_quantize": bench_rmsnorm_quantize,
+              "gdn_prefill": lambda *a: bench_gdn(wl.GDN_PREFILL, *a),
+              "gdn_decode": lambda *a: bench_gdn(wl.GDN_DECODE, *a)}[args.workload]
         print(json.dumps(fn(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return 0
     case = wl.ALL[args.workload]

@@ -16,8 +16,9 @@
  *      (Japanese article, "Mechanism 2").
  *
  * It also carries the companions of that layer on the same serving path: the FP8 E4M3 KV-cache
- * codec with static scales, the pages' own fold-in repair of the scale mismatch, and BF16 RMSNorm
- * fused with the quantizer (declared at the end of this file).
+ * codec with static scales, the pages' own fold-in repair of the scale mismatch, BF16 RMSNorm
+ * fused with the quantizer, and the Gated DeltaNet recurrence fed by the gates (declared at the end
+ * of this file).
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers; `stream` is a hipStream_t passed as void* (NULL means
@@ -232,6 +233,29 @@ const char* nvfp4_status_string(nvfp4_status s);
 
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char* nvfp4_last_error(void);
+
+/*
+ * nvfp4_gdn_recurrence -- the Gated DeltaNet delta-rule recurrence that consumes the gates of the
+ * fused in_proj GEMM (Japanese article, "How Gated DeltaNet works"; gates per "Mechanism 2"), in
+ * FP32 as in the pages' "FP32 lockstep" experiment ("Mechanism 3"). For each sequence b, value head
+ * h (key head h / (Hv / Hk)) and token t, with S the [D, D] state (key rows, value columns):
+ *   S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T,     o_t = S_t^T q_t
+ * (the update exactly as the pages write it; the readout is the usual linear-attention readout).
+ *   q_bf16, k_bf16: device bf16 [B*T, Hk*D], row r = b*T + t, strides ldq, ldk (elements), bases
+ *                   16-byte aligned, strides multiples of 8 elements (the GEMM's q and k segments);
+ *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment);
+ *   alpha, beta: device float [B*T, Hv], strides lda, ldb (the decay and write-strength gates, as the
+ *                GEMM's GDN_DECAY and SIGMOID epilogues write them);
+ *   state: device float [B, Hv, D, D], read as S_0 and overwritten with S_T;
+ *   o: device float [B*T, Hv*D], stride ldo.
+ * D must be 128; Hv must be a multiple of Hk. B == 0 or T == 0 is a no-op (state unchanged).
+ * Tokens are processed in order; sequences and heads in parallel. Deterministic.
+ * Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k_bf16, int64_t ldk,
+                                  const void* v_bf16, int64_t ldv, const float* alpha, int64_t lda,
+                                  const float* beta, int64_t ldb, float* state, int64_t B, int64_t T,
+                                  int32_t Hv, int32_t Hk, int32_t D, float* o, int64_t ldo, void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the library's HIP kern
 used for device memory and the current stream. The names mirror the C interface in
 include/nvfp4.h (nvfp4_global_scale, nvfp4_quantize, nvfp4_gemm, and the serving-path companions
 nvfp4_kv_scale / nvfp4_kv_quantize / nvfp4_kv_dequantize, nvfp4_fold_scales / nvfp4_fold_group,
-nvfp4_rmsnorm_quantize).
+nvfp4_rmsnorm_quantize, nvfp4_gdn_recurrence).
 
 If the library has not been built (``python -m nvfp4_w4a4_quantized_quantize_amd.build``), every
 call raises: there is no fallback implementation.
@@ -30,7 +30,8 @@ _EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
 # Every function the C header declares; a test checks the library exports all of them.
 EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
             "nvfp4_status_string", "nvfp4_last_error", "nvfp4_kv_scale", "nvfp4_kv_quantize",
-            "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize")
+            "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize",
+            "nvfp4_gdn_recurrence")
 
 
 class Nvfp4Error(RuntimeError):
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(f32), P]
         L.nvfp4_rmsnorm_quantize.restype = i32
         L.nvfp4_rmsnorm_quantize.argtypes = [P, i64, i64, i64, P, f32, f32, P, i64, P, i64, P, i64, P]
+        L.nvfp4_gdn_recurrence.restype = i32
+        L.nvfp4_gdn_recurrence.argtypes = [P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, i64, i32, i32, i32, P, i64, P]
         _lib = L
     return _lib
 
@@ -275,3 +278,26 @@ def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, g: float, cod
                                         _ld(codes, 16), _ptr(scales), _ld(scales, 16), _ptr(y), ldy,
                                         _stream(stream)), "nvfp4_rmsnorm_quantize")
     return codes, scales
+
+
+# ----------------------------------------------------------------- Gated DeltaNet recurrence
+def gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                   state: torch.Tensor, B: int, T: int, o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T, o_t = S_t^T q_t over B sequences of T tokens.
+
+    q, k: bf16 [B*T, Hk*128]; v: bf16 [B*T, Hv*128]; alpha, beta: float32 [B*T, Hv]; state: float32
+    [B, Hv, 128, 128], updated in place. Returns o float32 [B*T, Hv*128].
+    """
+    D = 128
+    for t in (q, k, v):
+        assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.stride(1) == 1 and t.shape[0] == B * T
+    for t in (alpha, beta):
+        assert t.dtype == torch.float32 and t.dim() == 2 and t.stride(1) == 1 and t.shape[0] == B * T
+    Hk, Hv = q.shape[1] // D, v.shape[1] // D
+    assert state.dtype == torch.float32 and state.is_contiguous() and tuple(state.shape) == (B, Hv, D, D)
+    if o is None:
+        o = torch.empty((B * T, Hv * D), dtype=torch.float32, device=q.device)
+    _check(lib().nvfp4_gdn_recurrence(_ptr(q), _ld(q, 8), _ptr(k), _ld(k, 8), _ptr(v), _ld(v, 1), _ptr(alpha),
+                                      _ld(alpha, 1), _ptr(beta), _ld(beta, 1), _ptr(state), B, T, Hv, Hk, D,
+                                      _ptr(o), _ld(o, 1), _stream(stream)), "nvfp4_gdn_recurrence")
+    return o

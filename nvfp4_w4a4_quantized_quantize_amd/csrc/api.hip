@@ -289,4 +289,30 @@ nvfp4_status nvfp4_rmsnorm_quantize(const void* x_bf16, int64_t rows, int64_t K,
                       "nvfp4_rmsnorm_quantize launch");
 }
 
+nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k_bf16, int64_t ldk, const void* v_bf16,
+                                  int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
+                                  float* state, int64_t B, int64_t T, int32_t Hv, int32_t Hk, int32_t D, float* o,
+                                  int64_t ldo, void* stream) {
+    if (B < 0 || T < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (D != 128) return fail(NVFP4_ERR_SHAPE, "head dimension D = %d is not supported (128)", D);
+    if (Hv < 1 || Hk < 1 || Hv % Hk != 0) return fail(NVFP4_ERR_SHAPE, "Hv = %d must be a positive multiple of Hk = %d", Hv, Hk);
+    if (B == 0 || T == 0) return ok();
+    if (!q_bf16 || !k_bf16 || !v_bf16 || !alpha || !beta || !state || !o)
+        return fail(NVFP4_ERR_NULL, "a GDN recurrence buffer is NULL");
+    if (ldq < (int64_t)Hk * D || ldk < (int64_t)Hk * D || ldv < (int64_t)Hv * D || lda < Hv || ldb < Hv ||
+        ldo < (int64_t)Hv * D)
+        return fail(NVFP4_ERR_SHAPE, "a row stride is smaller than its row");
+    if (!aligned16(q_bf16) || !aligned16(k_bf16) || ldq % 8 != 0 || ldk % 8 != 0)
+        return fail(NVFP4_ERR_ALIGN, "q and k must be 16-byte aligned with strides a multiple of 8 elements");
+    if ((reinterpret_cast<uintptr_t>(v_bf16) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
+        (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(state) & 3u) ||
+        (reinterpret_cast<uintptr_t>(o) & 3u))
+        return fail(NVFP4_ERR_ALIGN, "v, alpha, beta, state and o must be aligned to their element size");
+    return hip_status(nvfp4::launch_gdn_recurrence(static_cast<const uint16_t*>(q_bf16), ldq,
+                                                   static_cast<const uint16_t*>(k_bf16), ldk,
+                                                   static_cast<const uint16_t*>(v_bf16), ldv, alpha, lda, beta, ldb,
+                                                   state, B, T, Hv, Hk, o, ldo, static_cast<hipStream_t>(stream)),
+                      "nvfp4_gdn_recurrence launch");
+}
+
 }  // extern "C"

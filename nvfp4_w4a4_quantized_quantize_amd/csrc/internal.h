@@ -53,4 +53,9 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t K, i
                                    float eps, float g, uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
                                    uint16_t* y, int64_t ldy, hipStream_t stream);
 
+hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
+                                 int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
+                                 float* state, int64_t B, int64_t T, int32_t Hv, int32_t Hk, float* o, int64_t ldo,
+                                 hipStream_t stream);
+
 }  // namespace nvfp4

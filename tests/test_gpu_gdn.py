@@ -1,0 +1,93 @@
+"""GPU parity of the Gated DeltaNet recurrence (FP32 on the GPU) against the oracle (double).
+
+Tolerance: the GPU result must be within 8 times the error of the oracle's own float32 twin (the
+same recurrence in binary32, sequential sums) on the same input, plus 2^-22 of the output scale.
+Both are FP32 evaluations of a contractive recurrence (unit keys, decay and write strength in
+(0, 1]); they differ only in summation order, so their errors are of the same size."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_quantize_amd as nv
+import oracle
+import workloads as wl
+from gpu_common import DEV, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(q, k, v, alpha, beta, B, T, Hv, S0=None):
+    state = torch.zeros((B, Hv, 128, 128), dtype=torch.float32, device=DEV)
+    if S0 is not None:
+        state.copy_(torch.from_numpy(np.asarray(S0, np.float32)))
+    o = nv.gdn_recurrence(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(alpha).to(DEV),
+                          torch.from_numpy(beta).to(DEV), state, B, T)
+    return host(o).astype(np.float64), host(state).astype(np.float64)
+
+
+def check(o, S, q, k, v, alpha, beta, B, T, S0=None, what=""):
+    o64, S64 = oracle.gdn_recurrence(q, k, v, alpha, beta, B, T, S0=S0)
+    o32, S32 = oracle.gdn_recurrence(q, k, v, alpha, beta, B, T, S0=S0, f32=True)
+    for got, ref, twin, name in ((o, o64, o32, "o"), (S, S64, S32, "state")):
+        tol = 8 * np.abs(twin - ref).max() + 2.0 ** -22 * np.abs(ref).max()
+        err = np.abs(got - ref).max()
+        assert err <= tol, f"{what} {name}: max error {err:.3g} > tolerance {tol:.3g}"
+    return np.abs(o - o64).max() / max(np.abs(o64).max(), 1e-30)
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (2, 7), (1, 8), (3, 37), (1, 1000)])
+def test_small_shapes(B, T):
+    case = wl.GdnCase("t", 70, B, T, Hv=4, Hk=2)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, B, T, 4)
+    check(o, S, q, k, v, a, b, B, T, what=f"B={B} T={T}")
+
+
+def test_decode_step_batch_with_state():
+    """One decode step for 64 sequences, all 32 value heads, from a state built by 24 earlier tokens."""
+    case = wl.GDN_DECODE
+    q0, k0, v0, a0, b0 = wl.draw_gdn(case, seed=1, T=24)
+    _, S0 = oracle.gdn_recurrence(q0, k0, v0, a0, b0, case.B, 24)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, case.B, 1, case.Hv, S0=S0.astype(np.float32))
+    check(o, S, q, k, v, a, b, case.B, 1, S0=S0.astype(np.float32).astype(np.float64), what="decode")
+
+
+def test_state_carries_across_calls_bitwise():
+    case = wl.GdnCase("t", 71, 2, 40, Hv=4, Hk=2)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, 2, 40, 4)
+    # the same sequences in two calls of 19 and 21 tokens, carrying the state on the GPU
+    state = torch.zeros((2, 4, 128, 128), dtype=torch.float32, device=DEV)
+    sel = lambda x, lo, hi: np.concatenate([x[s * 40 + lo:s * 40 + hi] for s in range(2)])  # noqa: E731
+    outs = []
+    for lo, hi in ((0, 19), (19, 40)):
+        outs.append(host(nv.gdn_recurrence(dev_bf16(sel(q, lo, hi)), dev_bf16(sel(k, lo, hi)), dev_bf16(sel(v, lo, hi)),
+                                           torch.from_numpy(sel(a, lo, hi)).to(DEV),
+                                           torch.from_numpy(sel(b, lo, hi)).to(DEV), state, 2, hi - lo)))
+    o2 = np.concatenate([np.concatenate([outs[0][s * 19:(s + 1) * 19], outs[1][s * 21:(s + 1) * 21]]) for s in range(2)])
+    assert (o2 == o.astype(np.float32)).all() and (host(state) == S.astype(np.float32)).all()
+
+
+def test_inputs_as_slices_of_the_fused_projection_output():
+    """q, k, v as column slices of the fused in_proj output (row stride 12352) and the gates as the two
+    columns blocks of one [T, 64] FP32 buffer, exactly as the GEMM's segments would leave them."""
+    T = 50
+    case = wl.GdnCase("t", 72, 1, T)
+    q, k, v, a, b = wl.draw_gdn(case)
+    fused = torch.zeros((T, 12352), dtype=torch.bfloat16, device=DEV)
+    fused[:, :2048], fused[:, 2048:4096], fused[:, 4096:8192] = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    gates = torch.zeros((T, 64), dtype=torch.float32, device=DEV)
+    gates[:, :32], gates[:, 32:] = torch.from_numpy(b).to(DEV), torch.from_numpy(a).to(DEV)
+    state = torch.zeros((1, 32, 128, 128), dtype=torch.float32, device=DEV)
+    o = nv.gdn_recurrence(fused[:, :2048], fused[:, 2048:4096], fused[:, 4096:8192], gates[:, 32:], gates[:, :32],
+                          state, 1, T)
+    check(host(o).astype(np.float64), host(state).astype(np.float64), q, k, v, a, b, 1, T, what="slices")
+
+
+def test_prefill_8192_tokens_all_heads():
+    case = wl.GdnCase("t", 73, 1, 8192)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, 1, 8192, 32)
+    rel = check(o, S, q, k, v, a, b, 1, 8192, what="prefill 8192")
+    print(f"prefill 8192: max |o - exact| / max |o| = {rel:.3g}")
