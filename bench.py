@@ -35,14 +35,22 @@ PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 16.0  # read bf16, write codes + scales
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch recorded from rocprofv3 counters for this kernel source, else None."""
+def sources_digest(paths) -> str:
+    """sha256 over the given source files, in order (a kernel's file and the headers it includes)."""
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded from rocprofv3 counters for this kernel's sources, else None."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f)[kernel]
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            same = hashlib.sha256(f.read()).hexdigest() == rec["sha256"]
+        same = sources_digest(rec["sources"]) == rec["sha256"]
     except (OSError, KeyError, ValueError):
         return None
     if not same or rec["workload"] != workload:
