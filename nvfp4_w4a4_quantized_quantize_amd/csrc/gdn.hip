@@ -12,8 +12,9 @@
 // dot products over the key dimension are reduced inside a 16-lane row with DPP (quad swaps, then
 // row rotations by 4 and 8), so a wave needs no LDS and no barrier, and a workgroup of 4 waves
 // covers 16 columns. Token inputs (k, q: 16 bytes per lane; v; the gates) stream through an 8-token
-// register ring: each load is issued 8 tokens ahead and is unconditional (indices past T are
-// clamped), so the compiler waits for exactly one token's loads at a time.
+// register ring: each load is issued 8 tokens ahead and is unconditional (pointers that advance by
+// one row per token, clamped to the last token near the end), so the compiler waits for exactly one
+// token's loads at a time.
 #include <algorithm>
 
 #include "quant_common.h"
@@ -114,9 +115,35 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
     for (int i = 0; i < GDN_RING; ++i)
         load_token(ring[i], kp, qp, vp, ap, bp, std::min<int64_t>(i, T - 1), ldk, ldq, ldv, lda, ldb);
 
-    // full blocks of GDN_RING tokens: each step issues the loads of the token GDN_RING ahead (clamped
-    // to the last token), then computes; no condition in the body, so the waits stay exact
+    // Full blocks of GDN_RING tokens: each step issues the loads of the token GDN_RING ahead, then
+    // computes; no condition in the body, so the waits stay exact. While the token ahead is inside
+    // the sequence the load pointers just advance by one row per token (no index arithmetic); the
+    // last blocks clamp it to the last token.
     int64_t t0 = 0;
+    {
+        const uint16_t* kn = kp + GDN_RING * ldk;
+        const uint16_t* qn = qp + GDN_RING * ldq;
+        const uint16_t* vn = vp + GDN_RING * ldv;
+        const float* an = ap + GDN_RING * lda;
+        const float* bn = bp + GDN_RING * ldb;
+        float* ot = op;
+        for (; t0 + 2 * GDN_RING <= T; t0 += GDN_RING) {
+#pragma unroll
+            for (int i = 0; i < GDN_RING; ++i) {
+                const Token cur = ring[i];
+                load_token(ring[i], kn, qn, vn, an, bn, 0, 0, 0, 0, 0, 0);
+                kn += ldk;
+                qn += ldq;
+                vn += ldv;
+                an += lda;
+                bn += ldb;
+                __builtin_amdgcn_sched_barrier(0);
+                gdn_step(cur, S, kg, ot);
+                ot += ldo;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
     for (; t0 + GDN_RING <= T; t0 += GDN_RING) {
 #pragma unroll
         for (int i = 0; i < GDN_RING; ++i) {
