@@ -246,7 +246,9 @@ const char* nvfp4_last_error(void);
  *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment);
  *   alpha, beta: device float [B*T, Hv], strides lda, ldb (the decay and write-strength gates, as the
  *                GEMM's GDN_DECAY and SIGMOID epilogues write them);
- *   state: device float [B, Hv, D, D], read as S_0 and overwritten with S_T;
+ *   state: device float [B, Hv, D, D] holding each head's S value-major, i.e. S^T:
+ *          state[b][h][j][i] = S[i][j] (i key, j value), 16-byte aligned; read as S_0 and
+ *          overwritten with S_T;
  *   o: device float [B*T, Hv*D], stride ldo.
  * D must be 128; Hv must be a multiple of Hk. B == 0 or T == 0 is a no-op (state unchanged).
  * Tokens are processed in order; sequences and heads in parallel. Deterministic.

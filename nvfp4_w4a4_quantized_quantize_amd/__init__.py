@@ -286,7 +286,8 @@ def gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
     """S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T, o_t = S_t^T q_t over B sequences of T tokens.
 
     q, k: bf16 [B*T, Hk*128]; v: bf16 [B*T, Hv*128]; alpha, beta: float32 [B*T, Hv]; state: float32
-    [B, Hv, 128, 128], updated in place. Returns o float32 [B*T, Hv*128].
+    [B, Hv, 128, 128] holding each head's S value-major (state[b, h] = S^T), updated in place.
+    Returns o float32 [B*T, Hv*128].
     """
     D = 128
     for t in (q, k, v):

@@ -305,9 +305,9 @@ nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k
     if (!aligned16(q_bf16) || !aligned16(k_bf16) || ldq % 8 != 0 || ldk % 8 != 0)
         return fail(NVFP4_ERR_ALIGN, "q and k must be 16-byte aligned with strides a multiple of 8 elements");
     if ((reinterpret_cast<uintptr_t>(v_bf16) & 1u) || (reinterpret_cast<uintptr_t>(alpha) & 3u) ||
-        (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(state) & 3u) ||
-        (reinterpret_cast<uintptr_t>(o) & 3u))
-        return fail(NVFP4_ERR_ALIGN, "v, alpha, beta, state and o must be aligned to their element size");
+        (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(o) & 3u))
+        return fail(NVFP4_ERR_ALIGN, "v, alpha, beta and o must be aligned to their element size");
+    if (!aligned16(state)) return fail(NVFP4_ERR_ALIGN, "state must be 16-byte aligned");
     return hip_status(nvfp4::launch_gdn_recurrence(static_cast<const uint16_t*>(q_bf16), ldq,
                                                    static_cast<const uint16_t*>(k_bf16), ldk,
                                                    static_cast<const uint16_t*>(v_bf16), ldv, alpha, lda, beta, ldb,

@@ -4,15 +4,16 @@
 //
 // the delta-rule update of the paper arXiv:2609.04098 (Japanese article, "How Gated DeltaNet works"),
 // with the erase term as the pages write it (no alpha on it), in FP32 like the pages' "FP32 lockstep"
-// experiment ("Mechanism 3"). S is [D key, D value] per (sequence, value head); value head h reads
-// key head h / (Hv / Hk). The readout o_t = S_t^T q_t is the usual linear-attention readout.
+// experiment ("Mechanism 3"). S is [D key, D value] per (sequence, value head), stored value-major
+// (as S^T, one value column's key entries contiguous); value head h reads key head h / (Hv / Hk).
+// The readout o_t = S_t^T q_t is the usual linear-attention readout.
 //
 // Design: the value columns of S evolve independently (the delta rule couples key rows only), so a
 // wave owns 4 columns of one head's state, 8 key rows per lane: lane = 16 * column + row group. Both
 // dot products over the key dimension are reduced inside a 16-lane row with DPP (quad swaps, then
 // row rotations by 4 and 8), so a wave needs no LDS and no barrier, and a workgroup of 4 waves
 // covers 16 columns. Token inputs (k, q: 16 bytes per lane; v; the gates) stream through an 8-token
-// register ring: each load is issued 8 tokens ahead and is unconditional (pointers that advance by
+// register ring: each load is issued 8 tokens ahead (prefill) and is unconditional (pointers that advance by
 // one row per token, clamped to the last token near the end), so the compiler waits for exactly one
 // token's loads at a time.
 #include <algorithm>
@@ -22,8 +23,9 @@
 namespace nvfp4 {
 namespace {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int GDN_D = 128;    // head dimension (keys and values)
-constexpr int GDN_RING = 8;   // tokens in flight
 
 // Sum over the 16 lanes of a DPP row, returned in every lane of the row.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -78,6 +80,9 @@ __device__ __forceinline__ void gdn_step(const Token& cur, float (&S)[8], int kg
     if (kg == 0) *o_elem = oq;
 }
 
+// GDN_RING tokens in flight: 8 for prefill; 1 for decode-sized calls, where a deeper ring would only
+// reload the same few tokens and cost registers (occupancy).
+template <int GDN_RING>
 __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
     const uint16_t* __restrict__ v, int64_t ldv, const float* __restrict__ alpha, int64_t lda,
@@ -92,10 +97,17 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
     const int c = (int)(blockIdx.x % slices) * 16 + wave * 4 + (lane >> 4);  // value column
     const int hk = h / group;
 
-    float* Sp = state + bh * GDN_D * GDN_D + (int64_t)(8 * kg) * GDN_D + c;
+    // the state is stored value-major (S^T): this lane's 8 key rows of column c are contiguous
+    float* Sp = state + bh * GDN_D * GDN_D + (int64_t)c * GDN_D + 8 * kg;
     float S[8];
+    {
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(Sp), s1 = *reinterpret_cast<const f32x4_t*>(Sp + 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[i] = Sp[i * GDN_D];
+        for (int i = 0; i < 4; ++i) {
+            S[i] = s0[i];
+            S[4 + i] = s1[i];
+        }
+    }
 
     const int64_t r0 = b * T;  // first row of this sequence
     const uint16_t* kp = k + r0 * ldk + hk * GDN_D + 8 * kg;
@@ -159,8 +171,8 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 #pragma unroll
     for (int i = 0; i < GDN_RING - 1; ++i)
         if (t0 + i < T) gdn_step(ring[i], S, kg, op + (t0 + i) * ldo);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Sp[i * GDN_D] = S[i];
+    *reinterpret_cast<f32x4_t*>(Sp) = f32x4_t{S[0], S[1], S[2], S[3]};
+    *reinterpret_cast<f32x4_t*>(Sp + 4) = f32x4_t{S[4], S[5], S[6], S[7]};
 }
 
 }  // namespace
@@ -172,8 +184,8 @@ hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t*
     if (B == 0 || T == 0) return hipSuccess;
     const int64_t grid = B * Hv * (GDN_D / 16);
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gdn_recurrence_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, q, ldq, k, ldk, v, ldv,
-                       alpha, lda, beta, ldb, state, T, Hv, Hv / Hk, o, ldo);
+    hipLaunchKernelGGL(T >= 16 ? gdn_recurrence_kernel<8> : gdn_recurrence_kernel<1>, dim3((uint32_t)grid), dim3(256),
+                       0, stream, q, ldq, k, ldk, v, ldv, alpha, lda, beta, ldb, state, T, Hv, Hv / Hk, o, ldo);
     return hipGetLastError();
 }
 

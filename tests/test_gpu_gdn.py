@@ -16,13 +16,18 @@ from gpu_common import DEV, dev_bf16, host
 pytestmark = pytest.mark.gpu
 
 
+def to_value_major(S):
+    """[B, Hv, D key, D value] -> the library's value-major state layout (each head's S^T)."""
+    return np.ascontiguousarray(np.swapaxes(np.asarray(S), 2, 3))
+
+
 def run_gpu(q, k, v, alpha, beta, B, T, Hv, S0=None):
     state = torch.zeros((B, Hv, 128, 128), dtype=torch.float32, device=DEV)
     if S0 is not None:
-        state.copy_(torch.from_numpy(np.asarray(S0, np.float32)))
+        state.copy_(torch.from_numpy(to_value_major(np.asarray(S0, np.float32))))
     o = nv.gdn_recurrence(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(alpha).to(DEV),
                           torch.from_numpy(beta).to(DEV), state, B, T)
-    return host(o).astype(np.float64), host(state).astype(np.float64)
+    return host(o).astype(np.float64), to_value_major(host(state).astype(np.float64))
 
 
 def check(o, S, q, k, v, alpha, beta, B, T, S0=None, what=""):
@@ -66,7 +71,7 @@ def test_state_carries_across_calls_bitwise():
                                            torch.from_numpy(sel(a, lo, hi)).to(DEV),
                                            torch.from_numpy(sel(b, lo, hi)).to(DEV), state, 2, hi - lo)))
     o2 = np.concatenate([np.concatenate([outs[0][s * 19:(s + 1) * 19], outs[1][s * 21:(s + 1) * 21]]) for s in range(2)])
-    assert (o2 == o.astype(np.float32)).all() and (host(state) == S.astype(np.float32)).all()
+    assert (o2 == o.astype(np.float32)).all() and (to_value_major(host(state)) == S.astype(np.float32)).all()
 
 
 def test_inputs_as_slices_of_the_fused_projection_output():
@@ -82,7 +87,8 @@ def test_inputs_as_slices_of_the_fused_projection_output():
     state = torch.zeros((1, 32, 128, 128), dtype=torch.float32, device=DEV)
     o = nv.gdn_recurrence(fused[:, :2048], fused[:, 2048:4096], fused[:, 4096:8192], gates[:, 32:], gates[:, :32],
                           state, 1, T)
-    check(host(o).astype(np.float64), host(state).astype(np.float64), q, k, v, a, b, 1, T, what="slices")
+    check(host(o).astype(np.float64), to_value_major(host(state).astype(np.float64)), q, k, v, a, b, 1, T,
+          what="slices")
 
 
 def test_prefill_8192_tokens_all_heads():
