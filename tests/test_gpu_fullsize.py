@@ -13,7 +13,7 @@ import torch
 import nvfp4_w4a4_quantized_quantize_amd as nv
 import oracle
 import workloads as wl
-from gpu_common import DEV, check_bf16, check_decay, check_fp32, check_sigmoid, dev_bf16, host
+from gpu_common import DEV, check_bf16, check_decay, check_fp32, check_sigmoid, dev_bf16, host, padded_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,48 @@ def test_fused_mlp_gate_up():
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_fused_gdn_in_proj_32k(dtype):
     run_case(wl.C5, dtype, check_unfused=dtype == torch.bfloat16)
+
+
+def test_rmsnorm_quantize_full_size():
+    """RMSNorm + NVFP4 quantization of the full 32768 x 5120 activation, bit-exact with the oracle."""
+    case = wl.NORM
+    x, w = wl.draw_norm_x(case), wl.draw_norm_weight(case)
+    y_ref, _ = oracle.rmsnorm(x, w, np.float32(1e-6))
+    g = oracle.global_scale(y_ref)
+    c_ref, s_ref = oracle.quantize(y_ref, g)
+    print(f"{case.name}: GPU", flush=True)
+    codes, scales = nv.rmsnorm_quantize(dev_bf16(x), dev_bf16(w), 1e-6, float(g))
+    assert (host(codes) == c_ref).all() and (host(scales) == s_ref).all()
+
+
+def test_fold_in_repair_on_the_gdn_in_proj():
+    """The pages' own repair on the full GDN in_proj weights: folded scales bit-exact with the oracle;
+    the fused GEMM with the common scale against the exact per-segment result on sampled rows, which
+    must stay within 2^-4 of sum |a w| (the E4M3 re-rounding bound); the observed error is printed."""
+    case = wl.C5
+    M = 4096
+    x = wl.draw_x(case, M=M)
+    g_a = gpu_g(dev_bf16(x), x)
+    ac, as_ = oracle.quantize(x, g_a)
+    wcs, wss, gs = [], [], []
+    for s in range(len(case.segments)):
+        wb = wl.draw_w(case, s)
+        g = oracle.global_scale(wb)
+        c, sc = oracle.quantize(wb, g)
+        wcs.append(c)
+        wss.append(sc)
+        gs.append(g)
+    wc, ws = np.concatenate(wcs), np.concatenate(wss)
+    G_ref, folded = oracle.fold_group(wss, gs)
+    d_scales = padded_u8(ws)
+    G = nv.fold_group(d_scales, [s.n for s in case.segments], [float(g) for g in gs])
+    assert np.float32(G) == G_ref and (host(d_scales) == np.concatenate(folded)).all()
+    (out,) = nv.gemm(padded_u8(ac), padded_u8(as_), float(g_a), padded_u8(wc), d_scales, [nv.Segment(case.N, G)])
+    rows = sample_rows(x, M, 5)
+    y, T = oracle.gemm_rows(ac, as_, g_a, wc, ws, case.seg_bounds, np.array(gs, np.float32), rows)
+    got = host(out.index_select(0, torch.from_numpy(rows).to(DEV))).astype(np.float64)
+    err = np.abs(got - y)
+    assert (err <= (2.0 ** -4 + 2.0 ** -19) * T).all()
+    rel = np.linalg.norm(got - y) / np.linalg.norm(y)
+    print(f"fold-in vs per-segment scales on {len(rows)} rows: max |err|/T = {(err / T).max():.3g}, "
+          f"relative Frobenius error = {rel:.3g}", flush=True)
