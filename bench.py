@@ -248,6 +248,19 @@ def _time_loop(fn, n: int) -> float:
     return a.elapsed_time(b) / n
 
 
+def copy_ceiling_gbps(mb: int = 1024, reps: int = 10) -> float:
+    """Bytes moved (read + write) per second by a plain device-to-device copy of `mb` MiB: the
+    practical streaming ceiling of HBM on this machine, reported beside the nominal peak."""
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = _time_loop(lambda i: dst.copy_(src), reps)
+    del src, dst
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def bench_kv_cache(steps: int, warmup: int, cpu: bool) -> dict:
     """One step = the FP8 KV-cache write of a 32K-token prefill for every attention layer (K and V
     of 16 layers, each quantized with its own static scale), then the read of all of it back to
@@ -505,6 +518,8 @@ def main() -> int:
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,
                  "algorithmic_bytes": gemm_bytes})
     trq = measured_traffic("quantize_kernel", f"x_{M}x{K}")
+    copy_gbps = copy_ceiling_gbps()
+    log(f"[gpu] plain device copy: {copy_gbps:.0f} GB/s (read + write)")
     out = {
         "metric": "NVFP4 W4A4 GEMM TFLOPS at 32K-token prefill + quantize GB/s, % of roofline",
         "value": flops / (r["step_ms"] * 1e-3) / 1e12,
@@ -526,7 +541,8 @@ def main() -> int:
                               "frac": q_gbps / PEAK_HBM_GBPS, "traffic": trq[0] if trq else None,
                               "traffic_detail": trq[1] if trq else None, "kernel": "quantize_kernel",
                               "avg_ms": r["quant_iso_ms"], "avg_ms_in_step": r["quant_ms"],
-                              "algorithmic_bytes": q_bytes},
+                              "algorithmic_bytes": q_bytes, "copy_ceiling_gbps": copy_gbps,
+                              "frac_of_copy_ceiling": q_gbps / copy_gbps},
     }
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on a sample")
