@@ -26,6 +26,7 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GDN_D = 128;    // head dimension (keys and values)
+constexpr int64_t GDN_CHUNK_MIN_T = 32;  // calls with at least this many tokens take the chunked form
 
 // Sum over the 16 lanes of a DPP row, returned in every lane of the row.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -175,6 +176,343 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
     *reinterpret_cast<f32x4_t*>(Sp + 4) = f32x4_t{S[4], S[5], S[6], S[7]};
 }
 
+
+// ---------------------------------------------------------------------------------------------------
+// Chunked form, for prefill. Within a chunk of CH tokens starting from state S0, with
+// P(t, j) = prod_{j < i <= t} alpha_i and P(t, start) the product over the chunk up to t, the deltas
+// u_t = v_t - S_{t-1}^T k_t solve the unit lower-triangular system
+//     u_t + sum_{j < t} P(t-1, j) beta_j (k_t . k_j) u_j = v_t - P(t-1, start) S0^T k_t,
+// i.e. (I + L) U = R, and then
+//     o_t   = P(t, start) S0^T q_t + sum_{j <= t} P(t, j) beta_j (q_t . k_j) u_j     (O = G Q S0 + Mq U)
+//     S_end = P(end, start) S0 + sum_j P(end, j) beta_j k_j u_j^T.
+// This is the recurrence unrolled over the chunk, exact up to rounding. Each workgroup owns 16 value
+// columns of one head (the columns evolve independently) and walks the chunks in order, holding its
+// 128 x 16 slice of S in registers (FP32). The matrix products run on the matrix cores:
+//   * K K^T, K Q^T (bf16 inputs: the products are exact, FP32 sums): v_mfma_f32_16x16x32_bf16;
+//   * K S0, Q S0, K^T (w U): the FP32 operand is split into three bf16 parts x = h + m + l (each part
+//     the rounded remainder of the previous ones, so the sum carries 24 significant bits), which keeps
+//     FP32 accuracy at bf16 matrix rate;
+//   * T R, L U, Mq U (both operands FP32, 16 x 16 blocks): v_mfma_f32_16x16x4_f32.
+// The triangular system is solved by blocks of 16: T_bb = (I + L_bb)^-1 for the two diagonal blocks
+// by back substitution (VALU), then U_0 = T_00 R_0, U_1 = T_11 (R_1 - L_10 U_0).
+// The decay products P(t, j) are running products (robust to underflow, no logarithms). Tokens past
+// the end of the sequence are padded with k = q = v = 0, alpha = 1, beta = 0, which leave the state
+// unchanged. A chunk's inputs are loaded into registers one chunk ahead and staged in LDS (two buffers).
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 32;          // tokens per chunk
+constexpr int NV = 16;          // value columns per workgroup
+constexpr int KP = GDN_D + 8;   // LDS pitch (bf16) of a key / query row and of a state split row
+constexpr int FP = 36;          // LDS pitch (floats) of the 32-wide tables
+constexpr int WP = CH + 8;      // LDS pitch (bf16) of a w U split row
+
+struct ChunkLds {
+    __bf16 k[2][CH][KP];   // keys of the chunk (two buffers)
+    __bf16 q[2][CH][KP];   // queries
+    float v[2][NV][FP];    // the workgroup's value columns, value-major
+    float beta[2][CH];
+    float p[2][CH][FP];    // p[t][j] = P(t, j) for j <= t; p[t][32] = P(t, start)
+    float l[CH][FP];       // L, row-major (blocks 00, 10, 11)
+    float mq[CH][FP];      // Mq, row-major (blocks 00, 10, 11)
+    float ti[CH][FP];      // T_00 and T_11, row-major
+    float r[NV][FP];       // R, value-major
+    float u[NV][FP];       // U, value-major
+    __bf16 wu[3][NV][WP];  // P(end, j) beta_j U, split in three bf16 parts, value-major
+    __bf16 s[3][NV][KP];   // S split in three bf16 parts, value-major
+};
+
+struct ChunkIn {
+    qu32x4 k[2], q[2];  // 16-byte pieces tid and tid + 256 of the chunk: token piece / 16, keys 8 (piece % 16) ..
+    uint32_t v[2];     // value elements tid and tid + 256: token e / 16, column e % 16
+    float a, b;        // alpha, beta of token tid % 32
+};
+
+struct GdnIo {
+    const uint16_t *k, *q, *v;  // this workgroup's key head, query head, first value column (row 0 of its sequence)
+    const float *a, *b;         // its value head's gates
+    int64_t ldk, ldq, ldv, lda, ldb;
+};
+
+__device__ __forceinline__ f32x4_t mma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A 16 x 16 x 16 FP32 product: lane (g, r) supplies A[r][4g .. 4g + 3] and B[4g .. 4g + 3][r]; the
+// result lands as usual, lane (g, r) holding rows 4g .. 4g + 3 of column r (which is again the
+// B-operand layout of a following product).
+__device__ __forceinline__ f32x4_t mma16_f32(f32x4_t a, f32x4_t b, f32x4_t c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ void split3(f32x4_t x, bf16x4_t& h, bf16x4_t& m, bf16x4_t& l) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (__bf16)x[e];
+        const float r1 = x[e] - (float)h[e];
+        m[e] = (__bf16)r1;
+        l[e] = (__bf16)(r1 - (float)m[e]);
+    }
+}
+
+__device__ __forceinline__ void store_split(__bf16 (*dst)[NV][KP], int row, int col, f32x4_t x) {
+    bf16x4_t h, m, l;
+    split3(x, h, m, l);
+    *reinterpret_cast<bf16x4_t*>(&dst[0][row][col]) = h;
+    *reinterpret_cast<bf16x4_t*>(&dst[1][row][col]) = m;
+    *reinterpret_cast<bf16x4_t*>(&dst[2][row][col]) = l;
+}
+
+__device__ __forceinline__ void load_chunk(ChunkIn& in, const GdnIo& io, int64_t c0, int64_t T, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pc = tid + 256 * i;
+        const int64_t row = std::min<int64_t>(c0 + (pc >> 4), T - 1);
+        in.k[i] = *reinterpret_cast<const qu32x4*>(io.k + row * io.ldk + 8 * (pc & 15));
+        in.q[i] = *reinterpret_cast<const qu32x4*>(io.q + row * io.ldq + 8 * (pc & 15));
+        in.v[i] = io.v[row * io.ldv + (pc & 15)];
+    }
+    const int64_t row = std::min<int64_t>(c0 + (tid & 31), T - 1);
+    in.a = io.a[row * io.lda];
+    in.b = io.b[row * io.ldb];
+}
+
+// Writes a loaded chunk (n valid tokens) into LDS buffer bi; wave 1 builds its decay table.
+__device__ __forceinline__ void stage_chunk(ChunkLds& sm, int bi, const ChunkIn& in, int n, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pc = tid + 256 * i, t = pc >> 4, col = 8 * (pc & 15);
+        const bool ok = t < n;
+        const qu32x4 zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = ok ? in.k[i] : zero;
+        *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = ok ? in.q[i] : zero;
+        sm.v[bi][pc & 15][t] = ok ? bf16_lo(in.v[i]) : 0.0f;
+    }
+    if ((tid >> 6) == 1) {
+        const int lane = tid & 63, t = lane & 31;
+        const float a = t < n ? in.a : 1.0f;
+        if (lane < 32) sm.beta[bi][lane] = t < n ? in.b : 0.0f;
+        // lane j < 32: P(t, j), the product of alpha_i for j < i <= t; lane 32: P(t, start)
+        const int j = lane < 32 ? lane : -1;
+        float pr = 1.0f;
+#pragma unroll
+        for (int tt = 0; tt < CH; ++tt) {
+            const float at = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), tt));
+            if (tt > j) pr *= at;
+            if (lane <= 32) sm.p[bi][tt][lane] = pr;
+        }
+    }
+}
+
+// 16 x 16 tile of X K^T: lane (g, r) receives row t = 16 ti + r of X dotted with keys 16 tj + 4g + e.
+__device__ __forceinline__ f32x4_t gram_tile(const __bf16 (*kk)[KP], const __bf16 (*xx)[KP], int ti, int tj, int g,
+                                             int r) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < GDN_D / 32; ++ks)
+        acc = mma_bf16(*reinterpret_cast<const bf16x8_t*>(&kk[16 * tj + r][32 * ks + 8 * g]),
+                       *reinterpret_cast<const bf16x8_t*>(&xx[16 * ti + r][32 * ks + 8 * g]), acc);
+    return acc;
+}
+
+// L (strict: j < t, weight P(t-1, j) beta_j) or Mq (j <= t, weight P(t, j) beta_j) from a gram tile.
+template <bool STRICT>
+__device__ __forceinline__ void decay_tile(ChunkLds& sm, int bi, float (*dst)[FP], int ti, int tj, int g, int r,
+                                           f32x4_t x) {
+    const int t = 16 * ti + r, j0 = 16 * tj + 4 * g;
+    const int prow = STRICT ? (t > 0 ? t - 1 : 0) : t;
+    const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&sm.p[bi][prow][j0]);
+    const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&sm.beta[bi][j0]);
+    f32x4_t out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = (STRICT ? j0 + e < t : j0 + e <= t) ? pv[e] * bv[e] * x[e] : 0.0f;
+    *reinterpret_cast<f32x4_t*>(&dst[t][j0]) = out;
+}
+
+// T_bb = (I + L_bb)^-1 for diagonal block blk: lane (g, c) computes row c of T_bb by back substitution
+// (row c of T solves y (I + L) = e_c) and writes its columns 4g .. 4g + 3.
+__device__ __forceinline__ void invert_block(ChunkLds& sm, int blk, int g, int c) {
+    float y[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) y[t] = t == c ? 1.0f : 0.0f;
+#pragma unroll
+    for (int j = 15; j >= 1; --j) {
+        const float* lrow = &sm.l[16 * blk + j][16 * blk];
+        float lv[16];
+#pragma unroll
+        for (int q4 = 0; q4 < (j + 3) / 4; ++q4) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(lrow + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lv[4 * q4 + e] = x[e];
+        }
+#pragma unroll
+        for (int t = 0; t < j; ++t) y[t] = __builtin_fmaf(-y[j], lv[t], y[t]);
+    }
+    f32x4_t out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = g == 0 ? y[e] : g == 1 ? y[4 + e] : g == 2 ? y[8 + e] : y[12 + e];
+    *reinterpret_cast<f32x4_t*>(&sm.ti[16 * blk + c][16 * blk + 4 * g]) = out;
+}
+
+__global__ __launch_bounds__(256) void gdn_chunk_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
+    const uint16_t* __restrict__ v, int64_t ldv, const float* __restrict__ alpha, int64_t lda,
+    const float* __restrict__ beta, int64_t ldb, float* __restrict__ state, int64_t T, int32_t Hv, int32_t group,
+    float* __restrict__ o, int64_t ldo) {
+    __shared__ __attribute__((aligned(16))) ChunkLds sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+    constexpr int slices = GDN_D / NV;
+    const int64_t bh = blockIdx.x / slices;  // b * Hv + h
+    const int h = (int)(bh % Hv), slice = (int)(blockIdx.x % slices);
+    const int64_t b = bh / Hv, r0 = b * T;
+    const int hk = h / group;
+    const GdnIo io{k + r0 * ldk + hk * GDN_D, q + r0 * ldq + hk * GDN_D, v + r0 * ldv + h * GDN_D + slice * NV,
+                   alpha + r0 * lda + h, beta + r0 * ldb + h, ldk, ldq, ldv, lda, ldb};
+    float* ob = o + r0 * ldo + h * GDN_D + slice * NV;
+
+    // S rows (keys) 16 kt + 4g + e of column r, for this wave's key tiles kt = 2 wave, 2 wave + 1;
+    // stored value-major, so the four rows are contiguous
+    float* sg = state + bh * GDN_D * GDN_D + (int64_t)(slice * NV + r) * GDN_D + 32 * wave + 4 * g;
+    f32x4_t S[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        S[kk] = *reinterpret_cast<const f32x4_t*>(sg + 16 * kk);
+        store_split(sm.s, r, 32 * wave + 16 * kk + 4 * g, S[kk]);
+    }
+
+    const int64_t nch = (T + CH - 1) / CH;
+    ChunkIn in;
+    load_chunk(in, io, 0, T, tid);
+    stage_chunk(sm, 0, in, (int)std::min<int64_t>(CH, T), tid);
+    load_chunk(in, io, CH, T, tid);
+    __syncthreads();
+
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        const int bi = (int)(ch & 1);
+        const int64_t c0 = ch * CH;
+        const int n = (int)std::min<int64_t>(CH, T - c0);
+
+        // ---- phase 1: K S0 (waves 0, 1) or Q S0 (waves 2, 3) for token tile wave % 2; the L and Mq
+        // blocks; R = V - P(t-1, start) K S0
+        const int tt = wave & 1;
+        f32x4_t xs;
+        {
+            const __bf16 (*src)[KP] = wave < 2 ? sm.k[bi] : sm.q[bi];
+            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, a2 = a0;
+#pragma unroll
+            for (int ks = 0; ks < GDN_D / 32; ++ks) {
+                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&src[16 * tt + r][32 * ks + 8 * g]);
+                a0 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[0][r][32 * ks + 8 * g]), a0);
+                a1 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[1][r][32 * ks + 8 * g]), a1);
+                a2 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[2][r][32 * ks + 8 * g]), a2);
+            }
+            xs = (a2 + a1) + a0;
+        }
+        if (wave == 0) {
+            decay_tile<true>(sm, bi, sm.l, 0, 0, g, r, gram_tile(sm.k[bi], sm.k[bi], 0, 0, g, r));
+        } else if (wave == 1) {
+            decay_tile<true>(sm, bi, sm.l, 1, 0, g, r, gram_tile(sm.k[bi], sm.k[bi], 1, 0, g, r));
+        } else if (wave == 2) {
+            decay_tile<true>(sm, bi, sm.l, 1, 1, g, r, gram_tile(sm.k[bi], sm.k[bi], 1, 1, g, r));
+            decay_tile<false>(sm, bi, sm.mq, 0, 0, g, r, gram_tile(sm.k[bi], sm.q[bi], 0, 0, g, r));
+        } else {
+            decay_tile<false>(sm, bi, sm.mq, 1, 0, g, r, gram_tile(sm.k[bi], sm.q[bi], 1, 0, g, r));
+            decay_tile<false>(sm, bi, sm.mq, 1, 1, g, r, gram_tile(sm.k[bi], sm.q[bi], 1, 1, g, r));
+        }
+        if (wave < 2) {
+            const int t0 = 16 * tt + 4 * g;
+            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(&sm.v[bi][r][t0]);
+            f32x4_t rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = t0 + e;
+                const float gp = t > 0 ? sm.p[bi][t - 1][32] : 1.0f;
+                rr[e] = vv[e] - gp * xs[e];
+            }
+            *reinterpret_cast<f32x4_t*>(&sm.r[r][t0]) = rr;
+        }
+        __syncthreads();
+
+        // ---- phase 2: T_00, T_11
+        if (wave < 2) invert_block(sm, wave, g, r);
+        __syncthreads();
+
+        // ---- phase 3: U_0 = T_00 R_0, U_1 = T_11 (R_1 - L_10 U_0); U and w U to LDS
+        if (wave == 0) {
+            const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4_t R0 = *reinterpret_cast<const f32x4_t*>(&sm.r[r][4 * g]);
+            const f32x4_t R1 = *reinterpret_cast<const f32x4_t*>(&sm.r[r][16 + 4 * g]);
+            const f32x4_t U0 = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.ti[r][4 * g]), R0, zero);
+            const f32x4_t Y = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.l[16 + r][4 * g]), U0, zero);
+            const f32x4_t U1 = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.ti[16 + r][16 + 4 * g]), R1 - Y, zero);
+            *reinterpret_cast<f32x4_t*>(&sm.u[r][4 * g]) = U0;
+            *reinterpret_cast<f32x4_t*>(&sm.u[r][16 + 4 * g]) = U1;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t0 = 16 * half + 4 * g;
+                const f32x4_t pe = {sm.p[bi][CH - 1][t0], sm.p[bi][CH - 1][t0 + 1], sm.p[bi][CH - 1][t0 + 2],
+                                    sm.p[bi][CH - 1][t0 + 3]};
+                const f32x4_t be = *reinterpret_cast<const f32x4_t*>(&sm.beta[bi][t0]);
+                const f32x4_t uu = half ? U1 : U0;
+                const f32x4_t wu = (pe * be) * uu;
+                bf16x4_t hh, mm, ll;
+                split3(wu, hh, mm, ll);
+                *reinterpret_cast<bf16x4_t*>(&sm.wu[0][r][t0]) = hh;
+                *reinterpret_cast<bf16x4_t*>(&sm.wu[1][r][t0]) = mm;
+                *reinterpret_cast<bf16x4_t*>(&sm.wu[2][r][t0]) = ll;
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 4: outputs (waves 2, 3), S update (all), next chunk staged
+        if (wave >= 2) {
+            const int t0 = 16 * tt + 4 * g;
+            f32x4_t acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = sm.p[bi][t0 + e][32] * xs[e];
+            acc = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.mq[16 * tt + r][4 * g]),
+                            *reinterpret_cast<const f32x4_t*>(&sm.u[r][4 * g]), acc);
+            if (tt == 1)
+                acc = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.mq[16 + r][16 + 4 * g]),
+                                *reinterpret_cast<const f32x4_t*>(&sm.u[r][16 + 4 * g]), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t0 + e < n) ob[(c0 + t0 + e) * ldo + r] = acc[e];
+        }
+        {
+            const bf16x8_t B0 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[0][r][8 * g]);
+            const bf16x8_t B1 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[1][r][8 * g]);
+            const bf16x8_t B2 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[2][r][8 * g]);
+            const float gend = sm.p[bi][CH - 1][32];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int key = 32 * wave + 16 * kk + r;
+                bf16x8_t A;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) A[e] = sm.k[bi][8 * g + e][key];
+                f32x4_t acc = gend * S[kk];
+                acc = mma_bf16(A, B2, acc);
+                acc = mma_bf16(A, B1, acc);
+                acc = mma_bf16(A, B0, acc);
+                S[kk] = acc;
+            }
+        }
+        // the state split was last read in phase 1, buffer bi ^ 1 in the previous chunk
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) store_split(sm.s, r, 32 * wave + 16 * kk + 4 * g, S[kk]);
+        if (ch + 1 < nch) {
+            stage_chunk(sm, bi ^ 1, in, (int)std::min<int64_t>(CH, T - c0 - CH), tid);
+            load_chunk(in, io, c0 + 2 * CH, T, tid);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<f32x4_t*>(sg + 16 * kk) = S[kk];
+}
+
 }  // namespace
 
 hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
@@ -184,8 +522,13 @@ hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t*
     if (B == 0 || T == 0) return hipSuccess;
     const int64_t grid = B * Hv * (GDN_D / 16);
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(T >= 16 ? gdn_recurrence_kernel<8> : gdn_recurrence_kernel<1>, dim3((uint32_t)grid), dim3(256),
-                       0, stream, q, ldq, k, ldk, v, ldv, alpha, lda, beta, ldb, state, T, Hv, Hv / Hk, o, ldo);
+    if (T >= GDN_CHUNK_MIN_T)
+        hipLaunchKernelGGL(gdn_chunk_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, q, ldq, k, ldk, v, ldv, alpha,
+                           lda, beta, ldb, state, T, Hv, Hv / Hk, o, ldo);
+    else
+        hipLaunchKernelGGL(T >= 16 ? gdn_recurrence_kernel<8> : gdn_recurrence_kernel<1>, dim3((uint32_t)grid),
+                           dim3(256), 0, stream, q, ldq, k, ldk, v, ldv, alpha, lda, beta, ldb, state, T, Hv, Hv / Hk,
+                           o, ldo);
     return hipGetLastError();
 }
 

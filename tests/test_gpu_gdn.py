@@ -58,20 +58,88 @@ def test_decode_step_batch_with_state():
     check(o, S, q, k, v, a, b, case.B, 1, S0=S0.astype(np.float32).astype(np.float64), what="decode")
 
 
-def test_state_carries_across_calls_bitwise():
-    case = wl.GdnCase("t", 71, 2, 40, Hv=4, Hk=2)
+def run_split(q, k, v, a, b, B, T, Hv, cuts):
+    """The B sequences of T tokens fed in consecutive calls of the given lengths, carrying the state on
+    the GPU; returns the outputs re-assembled in [b][t] order and the final state."""
+    state = torch.zeros((B, Hv, 128, 128), dtype=torch.float32, device=DEV)
+    bounds = np.concatenate([[0], np.cumsum(cuts)])
+    assert bounds[-1] == T
+    sel = lambda x, lo, hi: np.concatenate([x[s * T + lo:s * T + hi] for s in range(B)])  # noqa: E731
+    parts = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        parts.append(host(nv.gdn_recurrence(dev_bf16(sel(q, lo, hi)), dev_bf16(sel(k, lo, hi)),
+                                            dev_bf16(sel(v, lo, hi)), torch.from_numpy(sel(a, lo, hi)).to(DEV),
+                                            torch.from_numpy(sel(b, lo, hi)).to(DEV), state, B, int(hi - lo))))
+    o = np.concatenate([np.concatenate([p[s * n:(s + 1) * n] for p, n in zip(parts, np.diff(bounds))])
+                        for s in range(B)])
+    return o, to_value_major(host(state))
+
+
+@pytest.mark.parametrize("T,cuts", [(24, (11, 13)), (96, (32, 64)), (128, (64, 32, 32))])
+def test_state_carries_across_calls_bitwise(T, cuts):
+    """Calls that split a sequence where the kernel's own blocking splits it give the same bits as one
+    call: under 32 tokens the token-by-token kernel, at chunk (32-token) boundaries the chunked one."""
+    case = wl.GdnCase("t", 71, 2, T, Hv=4, Hk=2)
     q, k, v, a, b = wl.draw_gdn(case)
-    o, S = run_gpu(q, k, v, a, b, 2, 40, 4)
-    # the same sequences in two calls of 19 and 21 tokens, carrying the state on the GPU
-    state = torch.zeros((2, 4, 128, 128), dtype=torch.float32, device=DEV)
-    sel = lambda x, lo, hi: np.concatenate([x[s * 40 + lo:s * 40 + hi] for s in range(2)])  # noqa: E731
-    outs = []
-    for lo, hi in ((0, 19), (19, 40)):
-        outs.append(host(nv.gdn_recurrence(dev_bf16(sel(q, lo, hi)), dev_bf16(sel(k, lo, hi)), dev_bf16(sel(v, lo, hi)),
-                                           torch.from_numpy(sel(a, lo, hi)).to(DEV),
-                                           torch.from_numpy(sel(b, lo, hi)).to(DEV), state, 2, hi - lo)))
-    o2 = np.concatenate([np.concatenate([outs[0][s * 19:(s + 1) * 19], outs[1][s * 21:(s + 1) * 21]]) for s in range(2)])
-    assert (o2 == o.astype(np.float32)).all() and (to_value_major(host(state)) == S.astype(np.float32)).all()
+    o, S = run_gpu(q, k, v, a, b, 2, T, 4)
+    o2, S2 = run_split(q, k, v, a, b, 2, T, 4, cuts)
+    assert (o2 == o.astype(np.float32)).all() and (S2 == S.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("cuts", [(19, 21), (1, 39), (33, 7)])
+def test_state_carries_across_calls(cuts):
+    """Any split (calls that take either kernel, chunks that start anywhere) meets the bound of one call."""
+    B, T = 2, 40
+    case = wl.GdnCase("t", 74, B, T, Hv=4, Hk=2)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_split(q, k, v, a, b, B, T, 4, cuts)
+    check(o.astype(np.float64), S.astype(np.float64), q, k, v, a, b, B, T, what=f"split {cuts}")
+
+
+@pytest.mark.parametrize("T", [32, 33, 63, 64, 65])
+def test_chunk_boundaries_from_a_state(T):
+    """Lengths around the 32-token chunk (one full chunk, a one-token tail, ...), two sequences, starting
+    from states built by 20 earlier tokens."""
+    B, Hv = 2, 4
+    case = wl.GdnCase("t", 75, B, T, Hv=Hv, Hk=2)
+    q0, k0, v0, a0, b0 = wl.draw_gdn(case, seed=5, T=20)
+    _, S0 = oracle.gdn_recurrence(q0, k0, v0, a0, b0, B, 20)
+    S0 = S0.astype(np.float32).astype(np.float64)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, B, T, Hv, S0=S0)
+    check(o, S, q, k, v, a, b, B, T, S0=S0, what=f"T={T}")
+
+
+@pytest.mark.parametrize("Hv,Hk", [(4, 4), (8, 2), (3, 1)])
+def test_chunked_head_grouping(Hv, Hk):
+    T = 70
+    case = wl.GdnCase("t", 76, 1, T, Hv=Hv, Hk=Hk)
+    q, k, v, a, b = wl.draw_gdn(case)
+    o, S = run_gpu(q, k, v, a, b, 1, T, Hv)
+    check(o, S, q, k, v, a, b, 1, T, what=f"Hv={Hv} Hk={Hk}")
+
+
+def test_chunked_extreme_gates_and_repeated_keys():
+    """Decays of exactly 0 and 1 and products that underflow inside a chunk (alpha = 1e-30), write
+    strengths 0 and 1, and runs of one repeated key (the delta rule then overwrites the same slot;
+    the triangular system has its largest off-diagonal weights)."""
+    B, T, Hv = 1, 96, 4
+    case = wl.GdnCase("t", 77, B, T, Hv=Hv, Hk=2)
+    q, k, v, a, b = wl.draw_gdn(case)
+    rng = np.random.default_rng(77)
+    a = a.copy()
+    b = b.copy()
+    a[rng.random(a.shape) < 0.05] = 0.0
+    a[rng.random(a.shape) < 0.05] = 1e-30
+    a[rng.random(a.shape) < 0.2] = 1.0
+    b[rng.random(b.shape) < 0.1] = 0.0
+    b[rng.random(b.shape) < 0.2] = 1.0
+    k = k.copy()
+    k[10:30] = k[10]
+    k[40:72:2] = k[40]
+    o, S = run_gpu(q, k, v, a, b, B, T, Hv)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    check(o, S, q, k, v, a, b, B, T, what="extreme gates")
 
 
 def test_inputs_as_slices_of_the_fused_projection_output():
