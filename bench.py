@@ -395,7 +395,9 @@ def bench_gdn(case, steps: int, warmup: int, cpu: bool) -> dict:
     copies = 1 if T > 1 else 4
     states = [torch.zeros((B, Hv, D, D), dtype=torch.float32, device="cuda") for _ in range(copies)]
     o = torch.empty((B * T, Hv * D), dtype=torch.float32, device="cuda")
-    run = lambda i: nv.gdn_recurrence(qd, kd, vd, ad, bd, states[i % copies], B, T, o=o)  # noqa: E731
+    need = nv.lib().nvfp4_gdn_workspace_bytes(B, T, Hv, case.Hk, D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    run = lambda i: nv.gdn_recurrence(qd, kd, vd, ad, bd, states[i % copies], B, T, o=o, workspace=ws)  # noqa: E731
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()

@@ -63,7 +63,7 @@ typedef enum {
     NVFP4_ERR_SEGMENTS = 4,  /* segment table empty, too long, unsorted, overlapping or not covering N */
     NVFP4_ERR_SCALE = 5,     /* a global scale is not finite and > 0 */
     NVFP4_ERR_EPILOGUE = 6,  /* unknown epilogue/out dtype, or a gate without FP32 output/parameters */
-    NVFP4_ERR_WORKSPACE = 7, /* workspace smaller than nvfp4_gemm_workspace_bytes() */
+    NVFP4_ERR_WORKSPACE = 7, /* workspace smaller than the call's *_workspace_bytes() */
     NVFP4_ERR_HIP = 8        /* the HIP runtime reported an error (launch failure, bad stream) */
 } nvfp4_status;
 
@@ -249,15 +249,26 @@ const char* nvfp4_last_error(void);
  *   state: device float [B, Hv, D, D] holding each head's S value-major, i.e. S^T:
  *          state[b][h][j][i] = S[i][j] (i key, j value), 16-byte aligned; read as S_0 and
  *          overwritten with S_T;
- *   o: device float [B*T, Hv*D], stride ldo.
+ *   o: device float [B*T, Hv*D], stride ldo;
+ *   workspace: device scratch of at least nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D) bytes, 16-byte
+ *              aligned (may be NULL when that is 0); its contents on entry do not matter.
  * D must be 128; Hv must be a multiple of Hk. B == 0 or T == 0 is a no-op (state unchanged).
+ * Calls of 32 tokens or more take the chunked form of the same recurrence (the article's chunked
+ * delta rule: within 32-token chunks the deltas solve a triangular system and the state advances
+ * once per chunk); shorter calls go token by token. Both compute in FP32 and differ only in rounding
+ * order; a call split at multiples of 32 tokens gives the same bits as the whole call.
  * Tokens are processed in order; sequences and heads in parallel. Deterministic.
- * Errors: NULL, SHAPE, ALIGN, HIP.
+ * Errors: NULL, SHAPE, ALIGN, WORKSPACE, HIP.
  */
 nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k_bf16, int64_t ldk,
                                   const void* v_bf16, int64_t ldv, const float* alpha, int64_t lda,
                                   const float* beta, int64_t ldb, float* state, int64_t B, int64_t T,
-                                  int32_t Hv, int32_t Hk, int32_t D, float* o, int64_t ldo, void* stream);
+                                  int32_t Hv, int32_t Hk, int32_t D, float* o, int64_t ldo, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace nvfp4_gdn_recurrence needs for this call (0 when none: token-by-token
+ * calls, or an invalid shape). */
+size_t nvfp4_gdn_workspace_bytes(int64_t B, int64_t T, int32_t Hv, int32_t Hk, int32_t D);
 
 #ifdef __cplusplus
 }

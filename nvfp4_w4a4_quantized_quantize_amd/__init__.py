@@ -31,7 +31,7 @@ _EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
 EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
             "nvfp4_status_string", "nvfp4_last_error", "nvfp4_kv_scale", "nvfp4_kv_quantize",
             "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize",
-            "nvfp4_gdn_recurrence")
+            "nvfp4_gdn_recurrence", "nvfp4_gdn_workspace_bytes")
 
 
 class Nvfp4Error(RuntimeError):
@@ -84,7 +84,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_rmsnorm_quantize.restype = i32
         L.nvfp4_rmsnorm_quantize.argtypes = [P, i64, i64, i64, P, f32, f32, P, i64, P, i64, P, i64, P]
         L.nvfp4_gdn_recurrence.restype = i32
-        L.nvfp4_gdn_recurrence.argtypes = [P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, i64, i32, i32, i32, P, i64, P]
+        L.nvfp4_gdn_recurrence.argtypes = [P, i64, P, i64, P, i64, P, i64, P, i64, P, i64, i64, i32, i32, i32, P, i64,
+                                           P, ctypes.c_size_t, P]
+        L.nvfp4_gdn_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_gdn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
         _lib = L
     return _lib
 
@@ -282,7 +285,8 @@ def rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, g: float, cod
 
 # ----------------------------------------------------------------- Gated DeltaNet recurrence
 def gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-                   state: torch.Tensor, B: int, T: int, o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                   state: torch.Tensor, B: int, T: int, o: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """S_t = alpha_t S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T, o_t = S_t^T q_t over B sequences of T tokens.
 
     q, k: bf16 [B*T, Hk*128]; v: bf16 [B*T, Hv*128]; alpha, beta: float32 [B*T, Hv]; state: float32
@@ -298,7 +302,12 @@ def gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
     assert state.dtype == torch.float32 and state.is_contiguous() and tuple(state.shape) == (B, Hv, D, D)
     if o is None:
         o = torch.empty((B * T, Hv * D), dtype=torch.float32, device=q.device)
+    need = lib().nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvfp4_gdn_recurrence(_ptr(q), _ld(q, 8), _ptr(k), _ld(k, 8), _ptr(v), _ld(v, 1), _ptr(alpha),
                                       _ld(alpha, 1), _ptr(beta), _ld(beta, 1), _ptr(state), B, T, Hv, Hk, D,
-                                      _ptr(o), _ld(o, 1), _stream(stream)), "nvfp4_gdn_recurrence")
+                                      _ptr(o), _ld(o, 1), _ptr(workspace), ws_bytes, _stream(stream)),
+           "nvfp4_gdn_recurrence")
     return o

@@ -289,10 +289,15 @@ nvfp4_status nvfp4_rmsnorm_quantize(const void* x_bf16, int64_t rows, int64_t K,
                       "nvfp4_rmsnorm_quantize launch");
 }
 
+size_t nvfp4_gdn_workspace_bytes(int64_t B, int64_t T, int32_t Hv, int32_t Hk, int32_t D) {
+    if (B <= 0 || T <= 0 || D != 128 || Hv < 1 || Hk < 1 || Hv % Hk != 0) return 0;
+    return nvfp4::gdn_workspace_bytes(B, T, Hv);
+}
+
 nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k_bf16, int64_t ldk, const void* v_bf16,
                                   int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
                                   float* state, int64_t B, int64_t T, int32_t Hv, int32_t Hk, int32_t D, float* o,
-                                  int64_t ldo, void* stream) {
+                                  int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || T < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
     if (D != 128) return fail(NVFP4_ERR_SHAPE, "head dimension D = %d is not supported (128)", D);
     if (Hv < 1 || Hk < 1 || Hv % Hk != 0) return fail(NVFP4_ERR_SHAPE, "Hv = %d must be a positive multiple of Hk = %d", Hv, Hk);
@@ -308,10 +313,15 @@ nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k
         (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(o) & 3u))
         return fail(NVFP4_ERR_ALIGN, "v, alpha, beta and o must be aligned to their element size");
     if (!aligned16(state)) return fail(NVFP4_ERR_ALIGN, "state must be 16-byte aligned");
+    const size_t need = nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
     return hip_status(nvfp4::launch_gdn_recurrence(static_cast<const uint16_t*>(q_bf16), ldq,
                                                    static_cast<const uint16_t*>(k_bf16), ldk,
                                                    static_cast<const uint16_t*>(v_bf16), ldv, alpha, lda, beta, ldb,
-                                                   state, B, T, Hv, Hk, o, ldo, static_cast<hipStream_t>(stream)),
+                                                   state, B, T, Hv, Hk, o, ldo, workspace,
+                                                   static_cast<hipStream_t>(stream)),
                       "nvfp4_gdn_recurrence launch");
 }
 

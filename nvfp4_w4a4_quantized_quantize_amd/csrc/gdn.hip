@@ -8,9 +8,12 @@
 // (as S^T, one value column's key entries contiguous); value head h reads key head h / (Hv / Hk).
 // The readout o_t = S_t^T q_t is the usual linear-attention readout.
 //
-// Design: the value columns of S evolve independently (the delta rule couples key rows only), so a
-// wave owns 4 columns of one head's state, 8 key rows per lane: lane = 16 * column + row group. Both
-// dot products over the key dimension are reduced inside a 16-lane row with DPP (quad swaps, then
+// Two forms of the same recurrence: token by token (decode-sized calls, below) and chunked (prefill,
+// further down), which the article names as the way the delta rule is trained and prefilled.
+//
+// Token by token: the value columns of S evolve independently (the delta rule couples key rows only),
+// so a wave owns 4 columns of one head's state, 8 key rows per lane: lane = 16 * column + row group.
+// Both dot products over the key dimension are reduced inside a 16-lane row with DPP (quad swaps, then
 // row rotations by 4 and 8), so a wave needs no LDS and no barrier, and a workgroup of 4 waves
 // covers 16 columns. Token inputs (k, q: 16 bytes per lane; v; the gates) stream through an 8-token
 // register ring: each load is issued 8 tokens ahead (prefill) and is unconditional (pointers that advance by
@@ -185,55 +188,42 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 // i.e. (I + L) U = R, and then
 //     o_t   = P(t, start) S0^T q_t + sum_{j <= t} P(t, j) beta_j (q_t . k_j) u_j     (O = G Q S0 + Mq U)
 //     S_end = P(end, start) S0 + sum_j P(end, j) beta_j k_j u_j^T.
-// This is the recurrence unrolled over the chunk, exact up to rounding. Each workgroup owns 16 value
-// columns of one head (the columns evolve independently) and walks the chunks in order, holding its
-// 128 x 16 slice of S in registers (FP32). The matrix products run on the matrix cores:
+// This is the recurrence unrolled over the chunk, exact up to rounding. Everything built from k, q,
+// alpha and beta alone (the decay products, T = (I + L)^-1, Mq and the gate vectors) does not depend
+// on the state; a first kernel computes it for every (sequence, value head, chunk) at once into the
+// caller's workspace. Only S0 -> R -> U -> S_end runs chunk after chunk, in a second kernel where each
+// workgroup owns 16 value columns of one head (the columns evolve independently) and holds its
+// 128 x 16 slice of S in registers (FP32), each of its four waves 32 key rows.
+// The matrix products run on the matrix cores:
 //   * K K^T, K Q^T (bf16 inputs: the products are exact, FP32 sums): v_mfma_f32_16x16x32_bf16;
 //   * K S0, Q S0, K^T (w U): the FP32 operand is split into three bf16 parts x = h + m + l (each part
 //     the rounded remainder of the previous ones, so the sum carries 24 significant bits), which keeps
 //     FP32 accuracy at bf16 matrix rate;
-//   * T R, L U, Mq U (both operands FP32, 16 x 16 blocks): v_mfma_f32_16x16x4_f32.
-// The triangular system is solved by blocks of 16: T_bb = (I + L_bb)^-1 for the two diagonal blocks
-// by back substitution (VALU), then U_0 = T_00 R_0, U_1 = T_11 (R_1 - L_10 U_0).
-// The decay products P(t, j) are running products (robust to underflow, no logarithms). Tokens past
-// the end of the sequence are padded with k = q = v = 0, alpha = 1, beta = 0, which leave the state
-// unchanged. A chunk's inputs are loaded into registers one chunk ahead and staged in LDS (two buffers).
+//   * T R, Mq U and the off-diagonal block of T (both operands FP32): v_mfma_f32_16x16x4_f32.
+// T is formed by 16-blocks: T_bb = (I + L_bb)^-1 by back substitution, T_10 = -T_11 L_10 T_00. The
+// decay products P(t, j) are running products (robust to underflow, no logarithms). Tokens past the
+// end of the sequence are padded with k = q = v = 0, alpha = 1, beta = 0, which leave the state
+// unchanged.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 32;          // tokens per chunk
-constexpr int NV = 16;          // value columns per workgroup
-constexpr int KP = GDN_D + 8;   // LDS pitch (bf16) of a key / query row and of a state split row
+constexpr int NV = 16;          // value columns per workgroup of the sequential kernel
+constexpr int KP = GDN_D + 8;   // LDS pitch (bf16) of a key / query row
 constexpr int FP = 36;          // LDS pitch (floats) of the 32-wide tables
 constexpr int WP = CH + 8;      // LDS pitch (bf16) of a w U split row
 
-struct ChunkLds {
-    __bf16 k[2][CH][KP];   // keys of the chunk (two buffers)
-    __bf16 q[2][CH][KP];   // queries
-    float v[2][NV][FP];    // the workgroup's value columns, value-major
-    float beta[2][CH];
-    float p[2][CH][FP];    // p[t][j] = P(t, j) for j <= t; p[t][32] = P(t, start)
-    float l[CH][FP];       // L, row-major (blocks 00, 10, 11)
-    float mq[CH][FP];      // Mq, row-major (blocks 00, 10, 11)
-    float ti[CH][FP];      // T_00 and T_11, row-major
-    float r[NV][FP];       // R, value-major
-    float u[NV][FP];       // U, value-major
-    __bf16 wu[3][NV][WP];  // P(end, j) beta_j U, split in three bf16 parts, value-major
-    __bf16 s[3][NV][KP];   // S split in three bf16 parts, value-major
+// What the sequential kernel needs of one chunk of one (sequence, value head), state aside.
+struct ChunkFactors {
+    float t[3][16][16];   // T = (I + L)^-1: blocks 00, 10, 11, row-major
+    float mq[3][16][16];  // Mq[t][j] = P(t, j) beta_j (q_t . k_j), j <= t: blocks 00, 10, 11
+    float gp[CH];         // P(t-1, start), the weight of S0^T k_t in R
+    float ga[CH];         // P(t, start), the weight of S0^T q_t in O
+    float w[CH];          // P(end, j) beta_j, the weight of k_j u_j^T in the state update
+    float gend[CH];       // [0]: P(end, start); the rest unused
 };
-
-struct ChunkIn {
-    qu32x4 k[2], q[2];  // 16-byte pieces tid and tid + 256 of the chunk: token piece / 16, keys 8 (piece % 16) ..
-    uint32_t v[2];     // value elements tid and tid + 256: token e / 16, column e % 16
-    float a, b;        // alpha, beta of token tid % 32
-};
-
-struct GdnIo {
-    const uint16_t *k, *q, *v;  // this workgroup's key head, query head, first value column (row 0 of its sequence)
-    const float *a, *b;         // its value head's gates
-    int64_t ldk, ldq, ldv, lda, ldb;
-};
+static_assert(sizeof(ChunkFactors) % 16 == 0, "chunk factors keep 16-byte alignment");
 
 __device__ __forceinline__ f32x4_t mma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -248,6 +238,8 @@ __device__ __forceinline__ f32x4_t mma16_f32(f32x4_t a, f32x4_t b, f32x4_t c) {
     return c;
 }
 
+__device__ __forceinline__ f32x4_t ld4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+
 __device__ __forceinline__ void split3(f32x4_t x, bf16x4_t& h, bf16x4_t& m, bf16x4_t& l) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -255,55 +247,6 @@ __device__ __forceinline__ void split3(f32x4_t x, bf16x4_t& h, bf16x4_t& m, bf16
         const float r1 = x[e] - (float)h[e];
         m[e] = (__bf16)r1;
         l[e] = (__bf16)(r1 - (float)m[e]);
-    }
-}
-
-__device__ __forceinline__ void store_split(__bf16 (*dst)[NV][KP], int row, int col, f32x4_t x) {
-    bf16x4_t h, m, l;
-    split3(x, h, m, l);
-    *reinterpret_cast<bf16x4_t*>(&dst[0][row][col]) = h;
-    *reinterpret_cast<bf16x4_t*>(&dst[1][row][col]) = m;
-    *reinterpret_cast<bf16x4_t*>(&dst[2][row][col]) = l;
-}
-
-__device__ __forceinline__ void load_chunk(ChunkIn& in, const GdnIo& io, int64_t c0, int64_t T, int tid) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pc = tid + 256 * i;
-        const int64_t row = std::min<int64_t>(c0 + (pc >> 4), T - 1);
-        in.k[i] = *reinterpret_cast<const qu32x4*>(io.k + row * io.ldk + 8 * (pc & 15));
-        in.q[i] = *reinterpret_cast<const qu32x4*>(io.q + row * io.ldq + 8 * (pc & 15));
-        in.v[i] = io.v[row * io.ldv + (pc & 15)];
-    }
-    const int64_t row = std::min<int64_t>(c0 + (tid & 31), T - 1);
-    in.a = io.a[row * io.lda];
-    in.b = io.b[row * io.ldb];
-}
-
-// Writes a loaded chunk (n valid tokens) into LDS buffer bi; wave 1 builds its decay table.
-__device__ __forceinline__ void stage_chunk(ChunkLds& sm, int bi, const ChunkIn& in, int n, int tid) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pc = tid + 256 * i, t = pc >> 4, col = 8 * (pc & 15);
-        const bool ok = t < n;
-        const qu32x4 zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = ok ? in.k[i] : zero;
-        *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = ok ? in.q[i] : zero;
-        sm.v[bi][pc & 15][t] = ok ? bf16_lo(in.v[i]) : 0.0f;
-    }
-    if ((tid >> 6) == 1) {
-        const int lane = tid & 63, t = lane & 31;
-        const float a = t < n ? in.a : 1.0f;
-        if (lane < 32) sm.beta[bi][lane] = t < n ? in.b : 0.0f;
-        // lane j < 32: P(t, j), the product of alpha_i for j < i <= t; lane 32: P(t, start)
-        const int j = lane < 32 ? lane : -1;
-        float pr = 1.0f;
-#pragma unroll
-        for (int tt = 0; tt < CH; ++tt) {
-            const float at = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), tt));
-            if (tt > j) pr *= at;
-            if (lane <= 32) sm.p[bi][tt][lane] = pr;
-        }
     }
 }
 
@@ -320,12 +263,11 @@ __device__ __forceinline__ f32x4_t gram_tile(const __bf16 (*kk)[KP], const __bf1
 
 // L (strict: j < t, weight P(t-1, j) beta_j) or Mq (j <= t, weight P(t, j) beta_j) from a gram tile.
 template <bool STRICT>
-__device__ __forceinline__ void decay_tile(ChunkLds& sm, int bi, float (*dst)[FP], int ti, int tj, int g, int r,
-                                           f32x4_t x) {
+__device__ __forceinline__ void decay_tile(const float (*p)[FP], const float* beta, float (*dst)[FP], int ti, int tj,
+                                           int g, int r, f32x4_t x) {
     const int t = 16 * ti + r, j0 = 16 * tj + 4 * g;
-    const int prow = STRICT ? (t > 0 ? t - 1 : 0) : t;
-    const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&sm.p[bi][prow][j0]);
-    const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&sm.beta[bi][j0]);
+    const f32x4_t pv = ld4(&p[STRICT ? (t > 0 ? t - 1 : 0) : t][j0]);
+    const f32x4_t bv = ld4(&beta[j0]);
     f32x4_t out;
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = (STRICT ? j0 + e < t : j0 + e <= t) ? pv[e] * bv[e] * x[e] : 0.0f;
@@ -333,202 +275,380 @@ __device__ __forceinline__ void decay_tile(ChunkLds& sm, int bi, float (*dst)[FP
 }
 
 // T_bb = (I + L_bb)^-1 for diagonal block blk: lane (g, c) computes row c of T_bb by back substitution
-// (row c of T solves y (I + L) = e_c) and writes its columns 4g .. 4g + 3.
-__device__ __forceinline__ void invert_block(ChunkLds& sm, int blk, int g, int c) {
+// (row c of T solves y (I + L) = e_c; y_t = 0 for t > c, y_c = 1); lanes of group 0 write it.
+__device__ __forceinline__ void invert_block(const float (*l)[FP], float (*ti)[FP], int blk, int g, int c) {
     float y[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) y[t] = t == c ? 1.0f : 0.0f;
+    for (int t = 0; t < 16; ++t) y[t] = 0.0f;
 #pragma unroll
     for (int j = 15; j >= 1; --j) {
-        const float* lrow = &sm.l[16 * blk + j][16 * blk];
-        float lv[16];
+        // y_j is final here: 1 at j = c, 0 above c, and below c complete after the updates from j + 1 ..
+        const float yv = j > c ? 0.0f : (j == c ? 1.0f : y[j]);
+        const float* lrow = &l[16 * blk + j][16 * blk];
 #pragma unroll
         for (int q4 = 0; q4 < (j + 3) / 4; ++q4) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(lrow + 4 * q4);
+            const f32x4_t x = ld4(lrow + 4 * q4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) lv[4 * q4 + e] = x[e];
+            for (int e = 0; e < 4; ++e)
+                if (4 * q4 + e < j) y[4 * q4 + e] = __builtin_fmaf(-yv, x[e], y[4 * q4 + e]);
         }
-#pragma unroll
-        for (int t = 0; t < j; ++t) y[t] = __builtin_fmaf(-y[j], lv[t], y[t]);
     }
-    f32x4_t out;
+    if (g == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = g == 0 ? y[e] : g == 1 ? y[4 + e] : g == 2 ? y[8 + e] : y[12 + e];
-    *reinterpret_cast<f32x4_t*>(&sm.ti[16 * blk + c][16 * blk + 4 * g]) = out;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4_t out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * q4 + e;
+                out[e] = t > c ? 0.0f : (t == c ? 1.0f : y[t]);
+            }
+            *reinterpret_cast<f32x4_t*>(&ti[16 * blk + c][16 * blk + 4 * q4]) = out;
+        }
+    }
+}
+
+struct PrepLds {
+    __bf16 k[CH][KP];
+    __bf16 q[CH][KP];
+    float p[CH][FP];  // p[t][j] = P(t, j) for j <= t; p[t][32] = P(t, start)
+    float beta[CH];
+    float l[CH][FP];   // L, row-major (blocks 00, 10, 11)
+    float mq[CH][FP];  // Mq, row-major (blocks 00, 10, 11)
+    float ti[CH][FP];  // T, row-major (blocks 00, 10, 11)
+};
+
+// One workgroup per (sequence, value head, chunk): blockIdx = (b Hv + h) nch + c.
+__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
+    const float* __restrict__ alpha, int64_t lda, const float* __restrict__ beta, int64_t ldb, int64_t T, int32_t Hv,
+    int32_t group, int64_t nch, ChunkFactors* __restrict__ fac) {
+    __shared__ __attribute__((aligned(16))) PrepLds sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+    const int64_t c = blockIdx.x % nch, bh = blockIdx.x / nch;
+    const int h = (int)(bh % Hv);
+    const int64_t b = bh / Hv, r0 = b * T, c0 = c * CH;
+    const int hk = h / group;
+    const int n = (int)std::min<int64_t>(CH, T - c0);
+    ChunkFactors* F = fac + blockIdx.x;
+
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int pc = tid + 256 * hh, t = pc >> 4, col = 8 * (pc & 15);
+        const int64_t row = r0 + std::min<int64_t>(c0 + t, T - 1);
+        const qu32x4 zero = {0u, 0u, 0u, 0u};
+        const qu32x4 kv = *reinterpret_cast<const qu32x4*>(k + row * ldk + hk * GDN_D + col);
+        const qu32x4 qv = *reinterpret_cast<const qu32x4*>(q + row * ldq + hk * GDN_D + col);
+        *reinterpret_cast<qu32x4*>(&sm.k[t][col]) = t < n ? kv : zero;
+        *reinterpret_cast<qu32x4*>(&sm.q[t][col]) = t < n ? qv : zero;
+    }
+    float a = 1.0f;
+    if (wave == 0) {
+        const int t = lane & 31;
+        const int64_t row = r0 + std::min<int64_t>(c0 + t, T - 1);
+        const float av = alpha[row * lda + h], bv = beta[row * ldb + h];
+        a = t < n ? av : 1.0f;
+        if (lane < 32) sm.beta[lane] = t < n ? bv : 0.0f;
+    }
+    __syncthreads();
+
+    f32x4_t G0, G1;
+    if (wave == 0) {
+        // lane j < 32: P(t, j), the product of alpha_i for j < i <= t; lane 32: P(t, start)
+        const int j = lane < 32 ? lane : -1;
+        float pr = 1.0f;
+#pragma unroll
+        for (int tt = 0; tt < CH; ++tt) {
+            const float at = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), tt));
+            if (tt > j) pr *= at;
+            if (lane <= 32) sm.p[tt][lane] = pr;
+        }
+    } else if (wave == 1) {
+        G0 = gram_tile(sm.k, sm.k, 0, 0, g, r);
+        G1 = gram_tile(sm.k, sm.k, 1, 0, g, r);
+    } else if (wave == 2) {
+        G0 = gram_tile(sm.k, sm.k, 1, 1, g, r);
+        G1 = gram_tile(sm.k, sm.q, 0, 0, g, r);
+    } else {
+        G0 = gram_tile(sm.k, sm.q, 1, 0, g, r);
+        G1 = gram_tile(sm.k, sm.q, 1, 1, g, r);
+    }
+    __syncthreads();
+
+    if (wave == 1) {
+        decay_tile<true>(sm.p, sm.beta, sm.l, 0, 0, g, r, G0);
+        decay_tile<true>(sm.p, sm.beta, sm.l, 1, 0, g, r, G1);
+    } else if (wave == 2) {
+        decay_tile<true>(sm.p, sm.beta, sm.l, 1, 1, g, r, G0);
+        decay_tile<false>(sm.p, sm.beta, sm.mq, 0, 0, g, r, G1);
+    } else if (wave == 3) {
+        decay_tile<false>(sm.p, sm.beta, sm.mq, 1, 0, g, r, G0);
+        decay_tile<false>(sm.p, sm.beta, sm.mq, 1, 1, g, r, G1);
+    } else if (lane < 32) {
+        const int t = lane;
+        F->gp[t] = t > 0 ? sm.p[t - 1][32] : 1.0f;
+        F->ga[t] = sm.p[t][32];
+        F->w[t] = sm.p[CH - 1][t] * sm.beta[t];
+        F->gend[t] = sm.p[CH - 1][32];
+    }
+    __syncthreads();
+
+    if (wave < 2) invert_block(sm.l, sm.ti, wave, g, r);
+    __syncthreads();
+
+    if (wave == 0) {  // T_10 = -T_11 (L_10 T_00)
+        const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x4_t t00 = {sm.ti[4 * g][r], sm.ti[4 * g + 1][r], sm.ti[4 * g + 2][r], sm.ti[4 * g + 3][r]};
+        const f32x4_t X = mma16_f32(ld4(&sm.l[16 + r][4 * g]), t00, zero);
+        const f32x4_t Y = mma16_f32(ld4(&sm.ti[16 + r][16 + 4 * g]), X, zero);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.ti[16 + 4 * g + e][r] = -Y[e];
+    }
+    __syncthreads();
+
+    // blocks 00, 10, 11 of T and Mq, 16 bytes per thread: piece = block * 64 + row * 4 + quarter
+    if (tid < 192) {
+        const int blk = tid >> 6, row = (tid >> 2) & 15, col = 4 * (tid & 3);
+        const int tr = 16 * (blk > 0) + row, tc = 16 * (blk == 2) + col;
+        *reinterpret_cast<f32x4_t*>(&F->t[blk][row][col]) = ld4(&sm.ti[tr][tc]);
+        *reinterpret_cast<f32x4_t*>(&F->mq[blk][row][col]) = ld4(&sm.mq[tr][tc]);
+    }
+}
+
+// The chunk factors a wave of the sequential kernel reads (loaded a chunk ahead).
+struct FactorRegs {
+    f32x4_t fa, fb;  // factor rows (T for waves 0, 1; Mq for waves 2, 3), columns 4g .. 4g + 3
+    f32x4_t g0, g1;  // waves 0, 1: gp at tokens 4g + e and 16 + 4g + e; waves 2, 3: ga at 16 tt + 4g + e
+    f32x4_t wt;      // w at tokens 16 tt + 4g + e
+    float gend;
+};
+
+// A chunk's keys, queries and value columns, 16-byte pieces i and i + 256 (token piece / 16, elements
+// 8 (piece % 16) ..), and value elements i, i + 256 (token e / 16, column e % 16).
+struct PieceRegs {
+    qu32x4 k[2], q[2];
+    uint32_t v[2];
+};
+
+struct MainLds {
+    __bf16 k[2][CH][KP];    // keys of chunks c and c + 1
+    __bf16 q[2][CH][KP];    // queries
+    float v[2][NV][FP];     // the workgroup's value columns, value-major
+    f32x4_t red[4][4][64];  // partial K S0 (tiles 0, 1) and Q S0 (tiles 0, 1) of each wave's key rows
+    float u[NV][FP];        // U, value-major
+    __bf16 wu[3][NV][WP];   // w U split in three bf16 parts, value-major
+};
+
+__device__ __forceinline__ void load_factors(FactorRegs& fr, const ChunkFactors* F, int wave, int g, int r,
+                                             int vzero) {
+    // wave 0: T_00; wave 1: T_10, T_11; wave 2: Mq_00; wave 3: Mq_10, Mq_11
+    const float* base = wave < 2 ? &F->t[0][0][0] : &F->mq[0][0][0];
+    const int ia = wave & 1, ib = (wave & 1) ? 2 : 0;
+    fr.fa = ld4(base + ia * 256 + 16 * r + 4 * g);
+    fr.fb = ld4(base + ib * 256 + 16 * r + 4 * g);
+    const int tt = wave & 1;
+    fr.g0 = ld4((wave < 2 ? F->gp : F->ga + 16 * tt) + 4 * g);
+    fr.g1 = ld4(F->gp + 16 + 4 * g);
+    fr.wt = ld4(F->w + 16 * tt + 4 * g);
+    fr.gend = F->gend[vzero];  // a vector load (see the note at the token-by-token kernel)
+}
+
+__device__ __forceinline__ void load_pieces(PieceRegs& pr, const uint16_t* kb, int64_t ldk, const uint16_t* qb,
+                                            int64_t ldq, const uint16_t* vb, int64_t ldv, int64_t c0, int64_t T,
+                                            int tid) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int pc = tid + 256 * hh;
+        const int64_t row = std::min<int64_t>(c0 + (pc >> 4), T - 1);
+        pr.k[hh] = *reinterpret_cast<const qu32x4*>(kb + row * ldk + 8 * (pc & 15));
+        pr.q[hh] = *reinterpret_cast<const qu32x4*>(qb + row * ldq + 8 * (pc & 15));
+        pr.v[hh] = vb[row * ldv + (pc & 15)];
+    }
+}
+
+__device__ __forceinline__ void stage_pieces(MainLds& sm, int bi, const PieceRegs& pr, int n, int tid) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int pc = tid + 256 * hh, t = pc >> 4, col = 8 * (pc & 15);
+        const bool ok = t < n;
+        const qu32x4 zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = ok ? pr.k[hh] : zero;
+        *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = ok ? pr.q[hh] : zero;
+        sm.v[bi][pc & 15][t] = ok ? bf16_lo(pr.v[hh]) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(qu32x2 lo, qu32x2 hi) {
+    const qu32x4 x = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8_t, x);
 }
 
 __global__ __launch_bounds__(256) void gdn_chunk_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
-    const uint16_t* __restrict__ v, int64_t ldv, const float* __restrict__ alpha, int64_t lda,
-    const float* __restrict__ beta, int64_t ldb, float* __restrict__ state, int64_t T, int32_t Hv, int32_t group,
-    float* __restrict__ o, int64_t ldo) {
-    __shared__ __attribute__((aligned(16))) ChunkLds sm;
+    const uint16_t* __restrict__ v, int64_t ldv, float* __restrict__ state, int64_t T, int32_t Hv, int32_t group,
+    int64_t nch, const ChunkFactors* __restrict__ fac, float* __restrict__ o, int64_t ldo) {
+    __shared__ __attribute__((aligned(16))) MainLds sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+    const int tt = wave & 1;
     constexpr int slices = GDN_D / NV;
     const int64_t bh = blockIdx.x / slices;  // b * Hv + h
     const int h = (int)(bh % Hv), slice = (int)(blockIdx.x % slices);
     const int64_t b = bh / Hv, r0 = b * T;
     const int hk = h / group;
-    const GdnIo io{k + r0 * ldk + hk * GDN_D, q + r0 * ldq + hk * GDN_D, v + r0 * ldv + h * GDN_D + slice * NV,
-                   alpha + r0 * lda + h, beta + r0 * ldb + h, ldk, ldq, ldv, lda, ldb};
+    const uint16_t* kb = k + r0 * ldk + hk * GDN_D;
+    const uint16_t* qb = q + r0 * ldq + hk * GDN_D;
+    const uint16_t* vb = v + r0 * ldv + h * GDN_D + slice * NV;
+    const ChunkFactors* Fh = fac + bh * nch;
     float* ob = o + r0 * ldo + h * GDN_D + slice * NV;
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
 
-    // S rows (keys) 16 kt + 4g + e of column r, for this wave's key tiles kt = 2 wave, 2 wave + 1;
-    // stored value-major, so the four rows are contiguous
+    // S rows (keys) 32 wave + 16 kk + 4g + e of column r; value-major in memory, so the four rows are
+    // contiguous
     float* sg = state + bh * GDN_D * GDN_D + (int64_t)(slice * NV + r) * GDN_D + 32 * wave + 4 * g;
-    f32x4_t S[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        S[kk] = *reinterpret_cast<const f32x4_t*>(sg + 16 * kk);
-        store_split(sm.s, r, 32 * wave + 16 * kk + 4 * g, S[kk]);
-    }
+    f32x4_t S[2] = {ld4(sg), ld4(sg + 16)};
 
-    const int64_t nch = (T + CH - 1) / CH;
-    ChunkIn in;
-    load_chunk(in, io, 0, T, tid);
-    stage_chunk(sm, 0, in, (int)std::min<int64_t>(CH, T), tid);
-    load_chunk(in, io, CH, T, tid);
+    auto valid = [&](int64_t c) { return (int)std::min<int64_t>(CH, T - c * CH); };
+    PieceRegs pieces;
+    load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, 0, T, tid);
+    stage_pieces(sm, 0, pieces, valid(0), tid);
+    load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, nch > 1 ? CH : 0, T, tid);
+    FactorRegs nxt;
+    load_factors(nxt, Fh, wave, g, r, vzero);
     __syncthreads();
 
-    for (int64_t ch = 0; ch < nch; ++ch) {
-        const int bi = (int)(ch & 1);
-        const int64_t c0 = ch * CH;
-        const int n = (int)std::min<int64_t>(CH, T - c0);
+    for (int64_t c = 0; c < nch; ++c) {
+        const int bi = (int)(c & 1);
+        const FactorRegs cur = nxt;
+        load_factors(nxt, Fh + (c + 1 < nch ? c + 1 : c), wave, g, r, vzero);
+        const int n = valid(c);
 
-        // ---- phase 1: K S0 (waves 0, 1) or Q S0 (waves 2, 3) for token tile wave % 2; the L and Mq
-        // blocks; R = V - P(t-1, start) K S0
-        const int tt = wave & 1;
-        f32x4_t xs;
+        // ---- phase 1: this wave's 32 key rows of K S0 and Q S0 for both token tiles. The matrix
+        // instruction's 8 k-slots of lane group g hold keys 32w + 4g + e and 32w + 16 + 4g + e, which are
+        // exactly the state rows the lane holds.
+        bf16x8_t B[3];
         {
-            const __bf16 (*src)[KP] = wave < 2 ? sm.k[bi] : sm.q[bi];
-            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, a2 = a0;
-#pragma unroll
-            for (int ks = 0; ks < GDN_D / 32; ++ks) {
-                const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&src[16 * tt + r][32 * ks + 8 * g]);
-                a0 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[0][r][32 * ks + 8 * g]), a0);
-                a1 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[1][r][32 * ks + 8 * g]), a1);
-                a2 = mma_bf16(A, *reinterpret_cast<const bf16x8_t*>(&sm.s[2][r][32 * ks + 8 * g]), a2);
-            }
-            xs = (a2 + a1) + a0;
-        }
-        if (wave == 0) {
-            decay_tile<true>(sm, bi, sm.l, 0, 0, g, r, gram_tile(sm.k[bi], sm.k[bi], 0, 0, g, r));
-        } else if (wave == 1) {
-            decay_tile<true>(sm, bi, sm.l, 1, 0, g, r, gram_tile(sm.k[bi], sm.k[bi], 1, 0, g, r));
-        } else if (wave == 2) {
-            decay_tile<true>(sm, bi, sm.l, 1, 1, g, r, gram_tile(sm.k[bi], sm.k[bi], 1, 1, g, r));
-            decay_tile<false>(sm, bi, sm.mq, 0, 0, g, r, gram_tile(sm.k[bi], sm.q[bi], 0, 0, g, r));
-        } else {
-            decay_tile<false>(sm, bi, sm.mq, 1, 0, g, r, gram_tile(sm.k[bi], sm.q[bi], 1, 0, g, r));
-            decay_tile<false>(sm, bi, sm.mq, 1, 1, g, r, gram_tile(sm.k[bi], sm.q[bi], 1, 1, g, r));
-        }
-        if (wave < 2) {
-            const int t0 = 16 * tt + 4 * g;
-            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(&sm.v[bi][r][t0]);
-            f32x4_t rr;
+            bf16x4_t h0, m0, l0, h1, m1, l1;
+            split3(S[0], h0, m0, l0);
+            split3(S[1], h1, m1, l1);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = t0 + e;
-                const float gp = t > 0 ? sm.p[bi][t - 1][32] : 1.0f;
-                rr[e] = vv[e] - gp * xs[e];
+                B[0][e] = h0[e];
+                B[0][4 + e] = h1[e];
+                B[1][e] = m0[e];
+                B[1][4 + e] = m1[e];
+                B[2][e] = l0[e];
+                B[2][4 + e] = l1[e];
             }
-            *reinterpret_cast<f32x4_t*>(&sm.r[r][t0]) = rr;
         }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const __bf16* row = x == 0 ? &sm.k[bi][16 * t2 + r][32 * wave + 4 * g]
+                                           : &sm.q[bi][16 * t2 + r][32 * wave + 4 * g];
+                const bf16x8_t A = as_bf16x8(*reinterpret_cast<const qu32x2*>(row),
+                                             *reinterpret_cast<const qu32x2*>(row + 16));
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                acc = mma_bf16(A, B[2], acc);
+                acc = mma_bf16(A, B[1], acc);
+                acc = mma_bf16(A, B[0], acc);
+                sm.red[wave][2 * x + t2][lane] = acc;
+            }
         __syncthreads();
 
-        // ---- phase 2: T_00, T_11
-        if (wave < 2) invert_block(sm, wave, g, r);
-        __syncthreads();
-
-        // ---- phase 3: U_0 = T_00 R_0, U_1 = T_11 (R_1 - L_10 U_0); U and w U to LDS
-        if (wave == 0) {
+        // ---- phase 2: waves 0, 1: R and U for token tile tt (U_0 = T_00 R_0, U_1 = T_10 R_0 + T_11 R_1);
+        // waves 2, 3: P(t, start) Q S0 for token tile tt. Then the next chunk is staged (its buffer was
+        // last read before the barrier above) and the one after it loaded.
+        f32x4_t xs;
+        if (wave < 2) {
+            f32x4_t R[2];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                if (t2 > tt) break;
+                const f32x4_t ks =
+                    ((sm.red[0][t2][lane] + sm.red[1][t2][lane]) + sm.red[2][t2][lane]) + sm.red[3][t2][lane];
+                const f32x4_t vv = ld4(&sm.v[bi][r][16 * t2 + 4 * g]);
+                R[t2] = vv - (t2 == 0 ? cur.g0 : cur.g1) * ks;
+            }
             const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            const f32x4_t R0 = *reinterpret_cast<const f32x4_t*>(&sm.r[r][4 * g]);
-            const f32x4_t R1 = *reinterpret_cast<const f32x4_t*>(&sm.r[r][16 + 4 * g]);
-            const f32x4_t U0 = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.ti[r][4 * g]), R0, zero);
-            const f32x4_t Y = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.l[16 + r][4 * g]), U0, zero);
-            const f32x4_t U1 = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.ti[16 + r][16 + 4 * g]), R1 - Y, zero);
-            *reinterpret_cast<f32x4_t*>(&sm.u[r][4 * g]) = U0;
-            *reinterpret_cast<f32x4_t*>(&sm.u[r][16 + 4 * g]) = U1;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int t0 = 16 * half + 4 * g;
-                const f32x4_t pe = {sm.p[bi][CH - 1][t0], sm.p[bi][CH - 1][t0 + 1], sm.p[bi][CH - 1][t0 + 2],
-                                    sm.p[bi][CH - 1][t0 + 3]};
-                const f32x4_t be = *reinterpret_cast<const f32x4_t*>(&sm.beta[bi][t0]);
-                const f32x4_t uu = half ? U1 : U0;
-                const f32x4_t wu = (pe * be) * uu;
-                bf16x4_t hh, mm, ll;
-                split3(wu, hh, mm, ll);
-                *reinterpret_cast<bf16x4_t*>(&sm.wu[0][r][t0]) = hh;
-                *reinterpret_cast<bf16x4_t*>(&sm.wu[1][r][t0]) = mm;
-                *reinterpret_cast<bf16x4_t*>(&sm.wu[2][r][t0]) = ll;
-            }
+            f32x4_t U = mma16_f32(cur.fa, R[0], zero);
+            if (tt == 1) U = mma16_f32(cur.fb, R[1], U);
+            const int t0 = 16 * tt + 4 * g;
+            *reinterpret_cast<f32x4_t*>(&sm.u[r][t0]) = U;
+            bf16x4_t hh, mm, ll;
+            split3(cur.wt * U, hh, mm, ll);
+            *reinterpret_cast<bf16x4_t*>(&sm.wu[0][r][t0]) = hh;
+            *reinterpret_cast<bf16x4_t*>(&sm.wu[1][r][t0]) = mm;
+            *reinterpret_cast<bf16x4_t*>(&sm.wu[2][r][t0]) = ll;
+        } else {
+            const f32x4_t qs = ((sm.red[0][2 + tt][lane] + sm.red[1][2 + tt][lane]) + sm.red[2][2 + tt][lane]) +
+                               sm.red[3][2 + tt][lane];
+            xs = cur.g0 * qs;
+        }
+        if (c + 1 < nch) {
+            stage_pieces(sm, bi ^ 1, pieces, valid(c + 1), tid);
+            load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, (c + 2 < nch ? c + 2 : c + 1) * CH, T, tid);
         }
         __syncthreads();
 
-        // ---- phase 4: outputs (waves 2, 3), S update (all), next chunk staged
+        // ---- phase 3: outputs (waves 2, 3) and the state update of each wave's key rows
         if (wave >= 2) {
+            f32x4_t acc = mma16_f32(cur.fa, ld4(&sm.u[r][4 * g]), xs);
+            if (tt == 1) acc = mma16_f32(cur.fb, ld4(&sm.u[r][16 + 4 * g]), acc);
             const int t0 = 16 * tt + 4 * g;
-            f32x4_t acc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = sm.p[bi][t0 + e][32] * xs[e];
-            acc = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.mq[16 * tt + r][4 * g]),
-                            *reinterpret_cast<const f32x4_t*>(&sm.u[r][4 * g]), acc);
-            if (tt == 1)
-                acc = mma16_f32(*reinterpret_cast<const f32x4_t*>(&sm.mq[16 + r][16 + 4 * g]),
-                                *reinterpret_cast<const f32x4_t*>(&sm.u[r][16 + 4 * g]), acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (t0 + e < n) ob[(c0 + t0 + e) * ldo + r] = acc[e];
+                if (t0 + e < n) ob[(c * CH + t0 + e) * ldo + r] = acc[e];
         }
         {
-            const bf16x8_t B0 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[0][r][8 * g]);
-            const bf16x8_t B1 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[1][r][8 * g]);
-            const bf16x8_t B2 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[2][r][8 * g]);
-            const float gend = sm.p[bi][CH - 1][32];
+            const bf16x8_t W0 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[0][r][8 * g]);
+            const bf16x8_t W1 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[1][r][8 * g]);
+            const bf16x8_t W2 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[2][r][8 * g]);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int key = 32 * wave + 16 * kk + r;
                 bf16x8_t A;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) A[e] = sm.k[bi][8 * g + e][key];
-                f32x4_t acc = gend * S[kk];
-                acc = mma_bf16(A, B2, acc);
-                acc = mma_bf16(A, B1, acc);
-                acc = mma_bf16(A, B0, acc);
+                f32x4_t acc = cur.gend * S[kk];
+                acc = mma_bf16(A, W2, acc);
+                acc = mma_bf16(A, W1, acc);
+                acc = mma_bf16(A, W0, acc);
                 S[kk] = acc;
             }
         }
-        // the state split was last read in phase 1, buffer bi ^ 1 in the previous chunk
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) store_split(sm.s, r, 32 * wave + 16 * kk + 4 * g, S[kk]);
-        if (ch + 1 < nch) {
-            stage_chunk(sm, bi ^ 1, in, (int)std::min<int64_t>(CH, T - c0 - CH), tid);
-            load_chunk(in, io, c0 + 2 * CH, T, tid);
-        }
-        __syncthreads();
     }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) *reinterpret_cast<f32x4_t*>(sg + 16 * kk) = S[kk];
+    *reinterpret_cast<f32x4_t*>(sg) = S[0];
+    *reinterpret_cast<f32x4_t*>(sg + 16) = S[1];
 }
 
 }  // namespace
 
+size_t gdn_workspace_bytes(int64_t B, int64_t T, int32_t Hv) {
+    if (B <= 0 || T < GDN_CHUNK_MIN_T || Hv <= 0) return 0;
+    return (size_t)B * (size_t)Hv * (size_t)((T + CH - 1) / CH) * sizeof(ChunkFactors);
+}
+
 hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
                                  int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
                                  float* state, int64_t B, int64_t T, int32_t Hv, int32_t Hk, float* o, int64_t ldo,
-                                 hipStream_t stream) {
+                                 void* workspace, hipStream_t stream) {
     if (B == 0 || T == 0) return hipSuccess;
     const int64_t grid = B * Hv * (GDN_D / 16);
     if (grid > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
-    if (T >= GDN_CHUNK_MIN_T)
-        hipLaunchKernelGGL(gdn_chunk_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, q, ldq, k, ldk, v, ldv, alpha,
-                           lda, beta, ldb, state, T, Hv, Hv / Hk, o, ldo);
-    else
+    if (T >= GDN_CHUNK_MIN_T) {
+        const int64_t nch = (T + CH - 1) / CH;
+        if (B * Hv * nch > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+        ChunkFactors* fac = static_cast<ChunkFactors*>(workspace);
+        hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((uint32_t)(B * Hv * nch)), dim3(256), 0, stream, q, ldq, k, ldk,
+                           alpha, lda, beta, ldb, T, Hv, Hv / Hk, nch, fac);
+        hipLaunchKernelGGL(gdn_chunk_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, q, ldq, k, ldk, v, ldv,
+                           state, T, Hv, Hv / Hk, nch, fac, o, ldo);
+    } else {
         hipLaunchKernelGGL(T >= 16 ? gdn_recurrence_kernel<8> : gdn_recurrence_kernel<1>, dim3((uint32_t)grid),
                            dim3(256), 0, stream, q, ldq, k, ldk, v, ldv, alpha, lda, beta, ldb, state, T, Hv, Hv / Hk,
                            o, ldo);
+    }
     return hipGetLastError();
 }
 

@@ -56,6 +56,8 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t rows, int64_t K, i
 hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk, const uint16_t* v,
                                  int64_t ldv, const float* alpha, int64_t lda, const float* beta, int64_t ldb,
                                  float* state, int64_t B, int64_t T, int32_t Hv, int32_t Hk, float* o, int64_t ldo,
-                                 hipStream_t stream);
+                                 void* workspace, hipStream_t stream);
+// Bytes of workspace launch_gdn_recurrence needs (the chunk factors of the chunked form; 0 below it).
+size_t gdn_workspace_bytes(int64_t B, int64_t T, int32_t Hv);
 
 }  // namespace nvfp4

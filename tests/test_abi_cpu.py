@@ -178,3 +178,37 @@ def rq(L, x=A16, rows=4, K=64, ldx=64, w=A16, eps=1e-6, g=1.0, codes=A16, ldc=32
 ])
 def test_rmsnorm_quantize_rejects(L, kw, status):
     assert rq(L, **kw) == status
+
+
+def gdn(L, q=A16, ldq=2048, k=A16, ldk=2048, v=A16, ldv=4096, a=A16, lda=32, b=A16, ldb=32, state=A16, B=1, T=64,
+        Hv=32, Hk=16, D=128, o=A16, ldo=4096, ws=A16, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D)
+    return L.nvfp4_gdn_recurrence(q, ldq, k, ldk, v, ldv, a, lda, b, ldb, state, B, T, Hv, Hk, D, o, ldo, ws,
+                                  ws_bytes, None)
+
+
+def test_gdn_workspace_bytes(L):
+    """The chunked form (32 tokens or more) keeps 6656 bytes of chunk factors per (sequence, value head,
+    32-token chunk); token-by-token calls and invalid shapes need none."""
+    W = L.nvfp4_gdn_workspace_bytes
+    assert W(1, 32768, 32, 16, 128) == 1024 * 32 * 6656
+    assert W(2, 33, 4, 2, 128) == 2 * 4 * 2 * 6656
+    assert W(64, 1, 32, 16, 128) == 0 and W(3, 31, 4, 2, 128) == 0
+    assert W(1, 64, 32, 16, 64) == 0 and W(1, 64, 30, 16, 128) == 0 and W(0, 64, 4, 2, 128) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(state=None), 1), (dict(o=None), 1),
+    (dict(D=64), 2), (dict(Hv=30), 2), (dict(T=-1), 2), (dict(ldv=4000), 2), (dict(lda=16), 2),
+    (dict(q=A16 + 8), 3), (dict(ldk=2052), 3), (dict(state=A16 + 4), 3), (dict(ws=A16 + 8), 3),
+    (dict(ws_bytes=1024), 7), (dict(ws=None), 7),
+])
+def test_gdn_rejects(L, kw, status):
+    assert gdn(L, **kw) == status
+    assert nv.last_error() != ""
+
+
+def test_gdn_empty_and_token_by_token_need_no_workspace(L):
+    assert gdn(L, B=0, ws=None, ws_bytes=0) == 0
+    assert gdn(L, T=0, ws=None, ws_bytes=0) == 0
