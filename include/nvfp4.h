@@ -243,7 +243,7 @@ const char* nvfp4_last_error(void);
  * (the update exactly as the pages write it; the readout is the usual linear-attention readout).
  *   q_bf16, k_bf16: device bf16 [B*T, Hk*D], row r = b*T + t, strides ldq, ldk (elements), bases
  *                   16-byte aligned, strides multiples of 8 elements (the GEMM's q and k segments);
- *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment);
+ *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment); ldq, ldk, ldv below 2^24;
  *   alpha, beta: device float [B*T, Hv], strides lda, ldb (the decay and write-strength gates, as the
  *                GEMM's GDN_DECAY and SIGMOID epilogues write them);
  *   state: device float [B, Hv, D, D] holding each head's S value-major, i.e. S^T:

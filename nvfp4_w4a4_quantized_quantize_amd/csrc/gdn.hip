@@ -422,11 +422,12 @@ struct FactorRegs {
     float gend;
 };
 
-// A chunk's keys, queries and value columns, 16-byte pieces i and i + 256 (token piece / 16, elements
-// 8 (piece % 16) ..), and value elements i, i + 256 (token e / 16, column e % 16).
+// A chunk's keys, queries and value columns as staged by waves 2 and 3 (thread i = 0 .. 127): 16-byte
+// pieces i + 128 m (token piece / 16, elements 8 (piece % 16) ..) and value elements i + 128 m (token
+// e / 16, column e % 16), m = 0 .. 3.
 struct PieceRegs {
-    qu32x4 k[2], q[2];
-    uint32_t v[2];
+    qu32x4 k[4], q[4];
+    uint32_t v[4];
 };
 
 struct MainLds {
@@ -452,28 +453,52 @@ __device__ __forceinline__ void load_factors(FactorRegs& fr, const ChunkFactors*
     fr.gend = F->gend[vzero];  // a vector load (see the note at the token-by-token kernel)
 }
 
-__device__ __forceinline__ void load_pieces(PieceRegs& pr, const uint16_t* kb, int64_t ldk, const uint16_t* qb,
-                                            int64_t ldq, const uint16_t* vb, int64_t ldv, int64_t c0, int64_t T,
-                                            int tid) {
+// Per-thread byte offsets of a staging thread's pieces inside a chunk (the same for every chunk).
+struct PieceOffs {
+    uint32_t k[4], q[4], v[4];
+};
+
+__device__ __forceinline__ PieceOffs piece_offsets(int64_t ldk, int64_t ldq, int64_t ldv, int i) {
+    PieceOffs po;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int pc = tid + 256 * hh;
-        const int64_t row = std::min<int64_t>(c0 + (pc >> 4), T - 1);
-        pr.k[hh] = *reinterpret_cast<const qu32x4*>(kb + row * ldk + 8 * (pc & 15));
-        pr.q[hh] = *reinterpret_cast<const qu32x4*>(qb + row * ldq + 8 * (pc & 15));
-        pr.v[hh] = vb[row * ldv + (pc & 15)];
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t t = (uint32_t)((i >> 4) + 8 * m);
+        po.k[m] = t * (uint32_t)ldk * 2u + 16u * (uint32_t)(i & 15);
+        po.q[m] = t * (uint32_t)ldq * 2u + 16u * (uint32_t)(i & 15);
+        po.v[m] = t * (uint32_t)ldv * 2u + 2u * (uint32_t)(i & 15);
+    }
+    return po;
+}
+
+// Buffer loads of chunk cl: each descriptor spans exactly the chunk's rows inside the sequence, so
+// the hardware returns zeros for the padding rows past the end (and for a chunk past the end).
+__device__ __forceinline__ void load_pieces(PieceRegs& pr, const PieceOffs& po, const uint16_t* kb, int64_t ldk,
+                                            const uint16_t* qb, int64_t ldq, const uint16_t* vb, int64_t ldv,
+                                            int64_t cl, int64_t T) {
+    const int64_t c0 = cl * CH;
+    const int64_t nv = std::max<int64_t>(0, std::min<int64_t>(CH, T - c0));
+    constexpr int FLAGS = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kb + c0 * ldk), (short)0, (int)(nv * ldk * 2), FLAGS);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qb + c0 * ldq), (short)0, (int)(nv * ldq * 2), FLAGS);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vb + c0 * ldv), (short)0, (int)(nv * ldv * 2), FLAGS);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        pr.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)po.k[m], 0, 0);
+        pr.q[m] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)po.q[m], 0, 0);
+        pr.v[m] = __builtin_amdgcn_raw_buffer_load_b16(rv, (int)po.v[m], 0, 0);
     }
 }
 
-__device__ __forceinline__ void stage_pieces(MainLds& sm, int bi, const PieceRegs& pr, int n, int tid) {
+__device__ __forceinline__ void stage_pieces(MainLds& sm, int bi, const PieceRegs& pr, int i) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int pc = tid + 256 * hh, t = pc >> 4, col = 8 * (pc & 15);
-        const bool ok = t < n;
-        const qu32x4 zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = ok ? pr.k[hh] : zero;
-        *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = ok ? pr.q[hh] : zero;
-        sm.v[bi][pc & 15][t] = ok ? bf16_lo(pr.v[hh]) : 0.0f;
+    for (int m = 0; m < 4; ++m) {
+        const int pc = i + 128 * m, t = pc >> 4, col = 8 * (pc & 15);
+        *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = pr.k[m];
+        *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = pr.q[m];
+        sm.v[bi][pc & 15][t] = bf16_lo(pr.v[m]);
     }
 }
 
@@ -485,13 +510,16 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(qu32x2 lo, qu32x2 hi) {
 __global__ __launch_bounds__(256) void gdn_chunk_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ k, int64_t ldk,
     const uint16_t* __restrict__ v, int64_t ldv, float* __restrict__ state, int64_t T, int32_t Hv, int32_t group,
-    int64_t nch, const ChunkFactors* __restrict__ fac, float* __restrict__ o, int64_t ldo) {
+    int64_t nch, int64_t nbh, const ChunkFactors* __restrict__ fac, float* __restrict__ o, int64_t ldo) {
     __shared__ __attribute__((aligned(16))) MainLds sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
     const int tt = wave & 1;
-    constexpr int slices = GDN_D / NV;
-    const int64_t bh = blockIdx.x / slices;  // b * Hv + h
-    const int h = (int)(bh % Hv), slice = (int)(blockIdx.x % slices);
+    // Workgroups are dealt to the 8 XCDs round-robin; the 8 value slices of one (sequence, head) go to
+    // one XCD (its L2 then serves their shared keys, queries and chunk factors, and whole value rows):
+    // workgroup i -> head 8 (i / 64) + i % 8, slice (i / 8) % 8. The grid is rounded up to 64.
+    const int64_t bh = 8 * (int64_t)(blockIdx.x / 64) + blockIdx.x % 8;  // b * Hv + h
+    if (bh >= nbh) return;
+    const int h = (int)(bh % Hv), slice = (int)((blockIdx.x / 8) % 8);
     const int64_t b = bh / Hv, r0 = b * T;
     const int hk = h / group;
     const uint16_t* kb = k + r0 * ldk + hk * GDN_D;
@@ -508,10 +536,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
     f32x4_t S[2] = {ld4(sg), ld4(sg + 16)};
 
     auto valid = [&](int64_t c) { return (int)std::min<int64_t>(CH, T - c * CH); };
+    // waves 2 and 3 stage the chunks (their phase 2 is the shorter one)
     PieceRegs pieces;
-    load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, 0, T, tid);
-    stage_pieces(sm, 0, pieces, valid(0), tid);
-    load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, nch > 1 ? CH : 0, T, tid);
+    const int si = tid - 128;
+    const PieceOffs po = piece_offsets(ldk, ldq, ldv, si);
+    if (wave >= 2) {
+        load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 0, T);
+        stage_pieces(sm, 0, pieces, si);
+        load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 1, T);
+    }
     FactorRegs nxt;
     load_factors(nxt, Fh, wave, g, r, vzero);
     __syncthreads();
@@ -584,11 +617,17 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
             const f32x4_t qs = ((sm.red[0][2 + tt][lane] + sm.red[1][2 + tt][lane]) + sm.red[2][2 + tt][lane]) +
                                sm.red[3][2 + tt][lane];
             xs = cur.g0 * qs;
+            // also past the end (zeros into the free buffer), so that the loads in flight are the same
+            // every iteration
+            stage_pieces(sm, bi ^ 1, pieces, si);
+            load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, c + 2, T);
         }
-        if (c + 1 < nch) {
-            stage_pieces(sm, bi ^ 1, pieces, valid(c + 1), tid);
-            load_pieces(pieces, kb, ldk, qb, ldq, vb, ldv, (c + 2 < nch ? c + 2 : c + 1) * CH, T, tid);
-        }
+        // the state update's K^T operands do not depend on this chunk's U: read them before the barrier
+        bf16x8_t KT[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) KT[kk][e] = sm.k[bi][8 * g + e][32 * wave + 16 * kk + r];
         __syncthreads();
 
         // ---- phase 3: outputs (waves 2, 3) and the state update of each wave's key rows
@@ -606,14 +645,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
             const bf16x8_t W2 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[2][r][8 * g]);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int key = 32 * wave + 16 * kk + r;
-                bf16x8_t A;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) A[e] = sm.k[bi][8 * g + e][key];
                 f32x4_t acc = cur.gend * S[kk];
-                acc = mma_bf16(A, W2, acc);
-                acc = mma_bf16(A, W1, acc);
-                acc = mma_bf16(A, W0, acc);
+                acc = mma_bf16(KT[kk], W2, acc);
+                acc = mma_bf16(KT[kk], W1, acc);
+                acc = mma_bf16(KT[kk], W0, acc);
                 S[kk] = acc;
             }
         }
@@ -642,8 +677,9 @@ hipError_t launch_gdn_recurrence(const uint16_t* q, int64_t ldq, const uint16_t*
         ChunkFactors* fac = static_cast<ChunkFactors*>(workspace);
         hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((uint32_t)(B * Hv * nch)), dim3(256), 0, stream, q, ldq, k, ldk,
                            alpha, lda, beta, ldb, T, Hv, Hv / Hk, nch, fac);
-        hipLaunchKernelGGL(gdn_chunk_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, q, ldq, k, ldk, v, ldv,
-                           state, T, Hv, Hv / Hk, nch, fac, o, ldo);
+        const int64_t nbh = B * Hv;
+        hipLaunchKernelGGL(gdn_chunk_kernel, dim3((uint32_t)((nbh + 7) / 8 * 64)), dim3(256), 0, stream, q, ldq, k,
+                           ldk, v, ldv, state, T, Hv, Hv / Hk, nch, nbh, fac, o, ldo);
     } else {
         hipLaunchKernelGGL(T >= 16 ? gdn_recurrence_kernel<8> : gdn_recurrence_kernel<1>, dim3((uint32_t)grid),
                            dim3(256), 0, stream, q, ldq, k, ldk, v, ldv, alpha, lda, beta, ldb, state, T, Hv, Hv / Hk,

@@ -201,6 +201,7 @@ def test_gdn_workspace_bytes(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(state=None), 1), (dict(o=None), 1),
     (dict(D=64), 2), (dict(Hv=30), 2), (dict(T=-1), 2), (dict(ldv=4000), 2), (dict(lda=16), 2),
+    (dict(ldv=1 << 24), 2),
     (dict(q=A16 + 8), 3), (dict(ldk=2052), 3), (dict(state=A16 + 4), 3), (dict(ws=A16 + 8), 3),
     (dict(ws_bytes=1024), 7), (dict(ws=None), 7),
 ])
