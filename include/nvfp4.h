@@ -253,10 +253,11 @@ const char* nvfp4_last_error(void);
  *   workspace: device scratch of at least nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D) bytes, 16-byte
  *              aligned (may be NULL when that is 0); its contents on entry do not matter.
  * D must be 128; Hv must be a multiple of Hk. B == 0 or T == 0 is a no-op (state unchanged).
- * Calls of 32 tokens or more take the chunked form of the same recurrence (the article's chunked
- * delta rule: within 32-token chunks the deltas solve a triangular system and the state advances
- * once per chunk); shorter calls go token by token. Both compute in FP32 and differ only in rounding
- * order; a call split at multiples of 32 tokens gives the same bits as the whole call.
+ * Calls of 32 tokens or more take the chunked form of the same recurrence (the update unrolled
+ * exactly over 32-token chunks: within a chunk the deltas v_t - S_{t-1}^T k_t solve a unit
+ * lower-triangular system and the state advances once per chunk); shorter calls go token by token.
+ * Both compute in FP32 and differ only in rounding order; a call split at multiples of 32 tokens
+ * gives the same bits as the whole call.
  * Tokens are processed in order; sequences and heads in parallel. Deterministic.
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, HIP.
  */

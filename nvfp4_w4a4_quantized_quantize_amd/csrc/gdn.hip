@@ -9,7 +9,8 @@
 // The readout o_t = S_t^T q_t is the usual linear-attention readout.
 //
 // Two forms of the same recurrence: token by token (decode-sized calls, below) and chunked (prefill,
-// further down), which the article names as the way the delta rule is trained and prefilled.
+// further down): the recurrence unrolled exactly over 32-token chunks, so that most of its work
+// becomes matrix products.
 //
 // Token by token: the value columns of S evolve independently (the delta rule couples key rows only),
 // so a wave owns 4 columns of one head's state, 8 key rows per lane: lane = 16 * column + row group.
