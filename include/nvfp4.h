@@ -243,7 +243,7 @@ const char* nvfp4_last_error(void);
  * (the update exactly as the pages write it; the readout is the usual linear-attention readout).
  *   q_bf16, k_bf16: device bf16 [B*T, Hk*D], row r = b*T + t, strides ldq, ldk (elements), bases
  *                   16-byte aligned, strides multiples of 8 elements (the GEMM's q and k segments);
- *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment); ldq, ldk, ldv below 2^24;
+ *   v_bf16: device bf16 [B*T, Hv*D], stride ldv (the v segment); ldq, ldk, ldv, ldo below 2^23;
  *   alpha, beta: device float [B*T, Hv], strides lda, ldb (the decay and write-strength gates, as the
  *                GEMM's GDN_DECAY and SIGMOID epilogues write them);
  *   state: device float [B, Hv, D, D] holding each head's S value-major, i.e. S^T:
@@ -254,9 +254,9 @@ const char* nvfp4_last_error(void);
  *              aligned (may be NULL when that is 0); its contents on entry do not matter.
  * D must be 128; Hv must be a multiple of Hk. B == 0 or T == 0 is a no-op (state unchanged).
  * Calls of 32 tokens or more take the chunked form of the same recurrence (the update unrolled
- * exactly over 32-token chunks: within a chunk the deltas v_t - S_{t-1}^T k_t solve a unit
+ * exactly over 64-token chunks: within a chunk the deltas v_t - S_{t-1}^T k_t solve a unit
  * lower-triangular system and the state advances once per chunk); shorter calls go token by token.
- * Both compute in FP32 and differ only in rounding order; a call split at multiples of 32 tokens
+ * Both compute in FP32 and differ only in rounding order; a call split at multiples of 64 tokens
  * gives the same bits as the whole call.
  * Tokens are processed in order; sequences and heads in parallel. Deterministic.
  * Errors: NULL, SHAPE, ALIGN, WORKSPACE, HIP.

@@ -313,8 +313,8 @@ nvfp4_status nvfp4_gdn_recurrence(const void* q_bf16, int64_t ldq, const void* k
         (reinterpret_cast<uintptr_t>(beta) & 3u) || (reinterpret_cast<uintptr_t>(o) & 3u))
         return fail(NVFP4_ERR_ALIGN, "v, alpha, beta and o must be aligned to their element size");
     if (!aligned16(state)) return fail(NVFP4_ERR_ALIGN, "state must be 16-byte aligned");
-    if (ldq >= (1 << 24) || ldk >= (1 << 24) || ldv >= (1 << 24))
-        return fail(NVFP4_ERR_SHAPE, "q, k and v row strides must be below 2^24 elements");
+    if (ldq >= (1 << 23) || ldk >= (1 << 23) || ldv >= (1 << 23) || ldo >= (1 << 23))
+        return fail(NVFP4_ERR_SHAPE, "q, k, v and o row strides must be below 2^23 elements");
     const size_t need = nvfp4_gdn_workspace_bytes(B, T, Hv, Hk, D);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);

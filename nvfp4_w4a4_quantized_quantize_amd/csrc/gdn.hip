@@ -209,20 +209,25 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int CH = 32;          // tokens per chunk
+constexpr int CH = 64;          // tokens per chunk
+constexpr int NTT = CH / 16;    // token tiles of 16 per chunk
 constexpr int NV = 16;          // value columns per workgroup of the sequential kernel
 constexpr int KP = GDN_D + 8;   // LDS pitch (bf16) of a key / query row
-constexpr int FP = 36;          // LDS pitch (floats) of the 32-wide tables
+constexpr int FP = CH + 4;      // LDS pitch (floats) of the chunk-wide tables (column CH: P(t, start))
 constexpr int WP = CH + 8;      // LDS pitch (bf16) of a w U split row
+constexpr int NBLK = NTT * (NTT + 1) / 2;  // 16 x 16 blocks on and below the diagonal
+
+// Lower-triangular 16-block (i, j), j <= i, stored at i (i + 1) / 2 + j.
+__host__ __device__ constexpr int blk(int i, int j) { return i * (i + 1) / 2 + j; }
 
 // What the sequential kernel needs of one chunk of one (sequence, value head), state aside.
 struct ChunkFactors {
-    float t[3][16][16];   // T = (I + L)^-1: blocks 00, 10, 11, row-major
-    float mq[3][16][16];  // Mq[t][j] = P(t, j) beta_j (q_t . k_j), j <= t: blocks 00, 10, 11
-    float gp[CH];         // P(t-1, start), the weight of S0^T k_t in R
-    float ga[CH];         // P(t, start), the weight of S0^T q_t in O
-    float w[CH];          // P(end, j) beta_j, the weight of k_j u_j^T in the state update
-    float gend[CH];       // [0]: P(end, start); the rest unused
+    float t[NBLK][16][16];   // T = (I + L)^-1: its lower blocks, row-major
+    float mq[NBLK][16][16];  // Mq[t][j] = P(t, j) beta_j (q_t . k_j), j <= t: lower blocks
+    float gp[CH];            // P(t-1, start), the weight of S0^T k_t in R
+    float ga[CH];            // P(t, start), the weight of S0^T q_t in O
+    float w[CH];             // P(end, j) beta_j, the weight of k_j u_j^T in the state update
+    float gend[CH];          // [0]: P(end, start); the rest unused
 };
 static_assert(sizeof(ChunkFactors) % 16 == 0, "chunk factors keep 16-byte alignment");
 
@@ -251,6 +256,12 @@ __device__ __forceinline__ void split3(f32x4_t x, bf16x4_t& h, bf16x4_t& m, bf16
     }
 }
 
+constexpr int BUF_FLAGS = 0x00020000;  // raw buffer resource, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, BUF_FLAGS);
+}
+
 // 16 x 16 tile of X K^T: lane (g, r) receives row t = 16 ti + r of X dotted with keys 16 tj + 4g + e.
 __device__ __forceinline__ f32x4_t gram_tile(const __bf16 (*kk)[KP], const __bf16 (*xx)[KP], int ti, int tj, int g,
                                              int r) {
@@ -263,21 +274,20 @@ __device__ __forceinline__ f32x4_t gram_tile(const __bf16 (*kk)[KP], const __bf1
 }
 
 // L (strict: j < t, weight P(t-1, j) beta_j) or Mq (j <= t, weight P(t, j) beta_j) from a gram tile.
-template <bool STRICT>
-__device__ __forceinline__ void decay_tile(const float (*p)[FP], const float* beta, float (*dst)[FP], int ti, int tj,
-                                           int g, int r, f32x4_t x) {
+__device__ __forceinline__ void decay_tile(const float (*p)[FP], const float* beta, float (*dst)[FP], bool strict,
+                                           int ti, int tj, int g, int r, f32x4_t x) {
     const int t = 16 * ti + r, j0 = 16 * tj + 4 * g;
-    const f32x4_t pv = ld4(&p[STRICT ? (t > 0 ? t - 1 : 0) : t][j0]);
+    const f32x4_t pv = ld4(&p[strict ? (t > 0 ? t - 1 : 0) : t][j0]);
     const f32x4_t bv = ld4(&beta[j0]);
     f32x4_t out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (STRICT ? j0 + e < t : j0 + e <= t) ? pv[e] * bv[e] * x[e] : 0.0f;
+    for (int e = 0; e < 4; ++e) out[e] = (strict ? j0 + e < t : j0 + e <= t) ? pv[e] * bv[e] * x[e] : 0.0f;
     *reinterpret_cast<f32x4_t*>(&dst[t][j0]) = out;
 }
 
-// T_bb = (I + L_bb)^-1 for diagonal block blk: lane (g, c) computes row c of T_bb by back substitution
+// T_bb = (I + L_bb)^-1 for diagonal block bb: lane (g, c) computes row c of T_bb by back substitution
 // (row c of T solves y (I + L) = e_c; y_t = 0 for t > c, y_c = 1); lanes of group 0 write it.
-__device__ __forceinline__ void invert_block(const float (*l)[FP], float (*ti)[FP], int blk, int g, int c) {
+__device__ __forceinline__ void invert_block(const float (*l)[FP], float (*ti)[FP], int bb, int g, int c) {
     float y[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) y[t] = 0.0f;
@@ -285,7 +295,7 @@ __device__ __forceinline__ void invert_block(const float (*l)[FP], float (*ti)[F
     for (int j = 15; j >= 1; --j) {
         // y_j is final here: 1 at j = c, 0 above c, and below c complete after the updates from j + 1 ..
         const float yv = j > c ? 0.0f : (j == c ? 1.0f : y[j]);
-        const float* lrow = &l[16 * blk + j][16 * blk];
+        const float* lrow = &l[16 * bb + j][16 * bb];
 #pragma unroll
         for (int q4 = 0; q4 < (j + 3) / 4; ++q4) {
             const f32x4_t x = ld4(lrow + 4 * q4);
@@ -303,19 +313,40 @@ __device__ __forceinline__ void invert_block(const float (*l)[FP], float (*ti)[F
                 const int t = 4 * q4 + e;
                 out[e] = t > c ? 0.0f : (t == c ? 1.0f : y[t]);
             }
-            *reinterpret_cast<f32x4_t*>(&ti[16 * blk + c][16 * blk + 4 * q4]) = out;
+            *reinterpret_cast<f32x4_t*>(&ti[16 * bb + c][16 * bb + 4 * q4]) = out;
         }
     }
 }
 
+// Off-diagonal block T_ij = -T_ii sum_{j <= k < i} L_ik T_kj (from (I + L) T = I, row block i).
+__device__ __forceinline__ void offdiag_block(const float (*l)[FP], float (*ti)[FP], int i, int j, int g, int r) {
+    f32x4_t X = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = j; k < i; ++k) {
+        const f32x4_t tkj = {ti[16 * k + 4 * g][16 * j + r], ti[16 * k + 4 * g + 1][16 * j + r],
+                             ti[16 * k + 4 * g + 2][16 * j + r], ti[16 * k + 4 * g + 3][16 * j + r]};
+        X = mma16_f32(ld4(&l[16 * i + r][16 * k + 4 * g]), tkj, X);
+    }
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t Y = mma16_f32(ld4(&ti[16 * i + r][16 * i + 4 * g]), X, zero);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ti[16 * i + 4 * g + e][16 * j + r] = -Y[e];
+}
+
+// Keys and queries are dead once the gram tiles are in registers, so L and T reuse their space
+// (about 52 KB in all: three workgroups per CU).
 struct PrepLds {
-    __bf16 k[CH][KP];
-    __bf16 q[CH][KP];
-    float p[CH][FP];  // p[t][j] = P(t, j) for j <= t; p[t][32] = P(t, start)
+    union {
+        struct {
+            __bf16 k[CH][KP];
+            __bf16 q[CH][KP];
+        } in;
+        struct {
+            float l[CH][FP];   // L, row-major (lower blocks)
+            float ti[CH][FP];  // T, row-major (lower blocks)
+        } tri;
+    };
+    float p[CH][FP];  // p[t][j] = P(t, j) for j <= t; p[t][CH] = P(t, start)
     float beta[CH];
-    float l[CH][FP];   // L, row-major (blocks 00, 10, 11)
-    float mq[CH][FP];  // Mq, row-major (blocks 00, 10, 11)
-    float ti[CH][FP];  // T, row-major (blocks 00, 10, 11)
 };
 
 // One workgroup per (sequence, value head, chunk): blockIdx = (b Hv + h) nch + c.
@@ -327,143 +358,162 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
     const int64_t c = blockIdx.x % nch, bh = blockIdx.x / nch;
     const int h = (int)(bh % Hv);
-    const int64_t b = bh / Hv, r0 = b * T, c0 = c * CH;
+    const int64_t b = bh / Hv, c0 = c * CH;
     const int hk = h / group;
     const int n = (int)std::min<int64_t>(CH, T - c0);
     ChunkFactors* F = fac + blockIdx.x;
 
+    // keys and queries of the chunk; rows past the sequence read as zeros (bounds-checked loads)
+    {
+        const int64_t row0 = b * T + c0;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(k + row0 * ldk + hk * GDN_D, (int64_t)n * ldk * 2);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q + row0 * ldq + hk * GDN_D, (int64_t)n * ldq * 2);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int pc = tid + 256 * hh, t = pc >> 4, col = 8 * (pc & 15);
-        const int64_t row = r0 + std::min<int64_t>(c0 + t, T - 1);
-        const qu32x4 zero = {0u, 0u, 0u, 0u};
-        const qu32x4 kv = *reinterpret_cast<const qu32x4*>(k + row * ldk + hk * GDN_D + col);
-        const qu32x4 qv = *reinterpret_cast<const qu32x4*>(q + row * ldq + hk * GDN_D + col);
-        *reinterpret_cast<qu32x4*>(&sm.k[t][col]) = t < n ? kv : zero;
-        *reinterpret_cast<qu32x4*>(&sm.q[t][col]) = t < n ? qv : zero;
+        for (int m = 0; m < CH * 16 / 256; ++m) {
+            const int pc = tid + 256 * m, t = pc >> 4, col = 8 * (pc & 15);
+            *reinterpret_cast<qu32x4*>(&sm.in.k[t][col]) =
+                __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(t * (uint32_t)ldk * 2u + 2u * col), 0, 0);
+            *reinterpret_cast<qu32x4*>(&sm.in.q[t][col]) =
+                __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(t * (uint32_t)ldq * 2u + 2u * col), 0, 0);
+        }
     }
     float a = 1.0f;
-    if (wave == 0) {
-        const int t = lane & 31;
-        const int64_t row = r0 + std::min<int64_t>(c0 + t, T - 1);
+    if (wave == 0) {  // lane t: alpha_t, beta_t (padding: alpha 1, beta 0)
+        const int64_t row = b * T + std::min<int64_t>(c0 + lane, T - 1);
         const float av = alpha[row * lda + h], bv = beta[row * ldb + h];
-        a = t < n ? av : 1.0f;
-        if (lane < 32) sm.beta[lane] = t < n ? bv : 0.0f;
+        a = lane < n ? av : 1.0f;
+        sm.beta[lane] = lane < n ? bv : 0.0f;
     }
     __syncthreads();
 
-    f32x4_t G0, G1;
+    // wave 0: decay table; waves 1-3: the 20 gram tiles (10 of K K^T for L, 10 of K Q^T for Mq)
+    constexpr int JOBS_PER_WAVE = 7;
+    f32x4_t G[JOBS_PER_WAVE];
     if (wave == 0) {
-        // lane j < 32: P(t, j), the product of alpha_i for j < i <= t; lane 32: P(t, start)
-        const int j = lane < 32 ? lane : -1;
+        // lane j: P(t, j), the product of alpha_i for j < i <= t
         float pr = 1.0f;
 #pragma unroll
         for (int tt = 0; tt < CH; ++tt) {
             const float at = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), tt));
-            if (tt > j) pr *= at;
-            if (lane <= 32) sm.p[tt][lane] = pr;
+            if (tt > lane) pr *= at;
+            sm.p[tt][lane] = pr;
         }
-    } else if (wave == 1) {
-        G0 = gram_tile(sm.k, sm.k, 0, 0, g, r);
-        G1 = gram_tile(sm.k, sm.k, 1, 0, g, r);
-    } else if (wave == 2) {
-        G0 = gram_tile(sm.k, sm.k, 1, 1, g, r);
-        G1 = gram_tile(sm.k, sm.q, 0, 0, g, r);
+        // P(t, start) = alpha_0 P(t, 0)
+        const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0));
+        sm.p[lane][CH] = a0 * sm.p[lane][0];
     } else {
-        G0 = gram_tile(sm.k, sm.q, 1, 0, g, r);
-        G1 = gram_tile(sm.k, sm.q, 1, 1, g, r);
-    }
-    __syncthreads();
-
-    if (wave == 1) {
-        decay_tile<true>(sm.p, sm.beta, sm.l, 0, 0, g, r, G0);
-        decay_tile<true>(sm.p, sm.beta, sm.l, 1, 0, g, r, G1);
-    } else if (wave == 2) {
-        decay_tile<true>(sm.p, sm.beta, sm.l, 1, 1, g, r, G0);
-        decay_tile<false>(sm.p, sm.beta, sm.mq, 0, 0, g, r, G1);
-    } else if (wave == 3) {
-        decay_tile<false>(sm.p, sm.beta, sm.mq, 1, 0, g, r, G0);
-        decay_tile<false>(sm.p, sm.beta, sm.mq, 1, 1, g, r, G1);
-    } else if (lane < 32) {
-        const int t = lane;
-        F->gp[t] = t > 0 ? sm.p[t - 1][32] : 1.0f;
-        F->ga[t] = sm.p[t][32];
-        F->w[t] = sm.p[CH - 1][t] * sm.beta[t];
-        F->gend[t] = sm.p[CH - 1][32];
-    }
-    __syncthreads();
-
-    if (wave < 2) invert_block(sm.l, sm.ti, wave, g, r);
-    __syncthreads();
-
-    if (wave == 0) {  // T_10 = -T_11 (L_10 T_00)
-        const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const f32x4_t t00 = {sm.ti[4 * g][r], sm.ti[4 * g + 1][r], sm.ti[4 * g + 2][r], sm.ti[4 * g + 3][r]};
-        const f32x4_t X = mma16_f32(ld4(&sm.l[16 + r][4 * g]), t00, zero);
-        const f32x4_t Y = mma16_f32(ld4(&sm.ti[16 + r][16 + 4 * g]), X, zero);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.ti[16 + 4 * g + e][r] = -Y[e];
+        for (int s = 0; s < JOBS_PER_WAVE; ++s) {
+            const int job = JOBS_PER_WAVE * (wave - 1) + s;
+            if (job < 2 * NBLK) {
+                const int tri = job % NBLK;
+                const int ti = tri >= 6 ? 3 : tri >= 3 ? 2 : tri >= 1 ? 1 : 0, tj = tri - blk(ti, 0);
+                G[s] = gram_tile(sm.in.k, job < NBLK ? sm.in.k : sm.in.q, ti, tj, g, r);
+            }
+        }
+    }
+    __syncthreads();  // every gram tile is in registers: the key and query space is free
+
+    if (wave == 0) {
+        F->gp[lane] = lane > 0 ? sm.p[lane - 1][CH] : 1.0f;
+        F->ga[lane] = sm.p[lane][CH];
+        F->w[lane] = sm.p[CH - 1][lane] * sm.beta[lane];
+        F->gend[lane] = sm.p[CH - 1][CH];
+    } else {
+#pragma unroll
+        for (int s = 0; s < JOBS_PER_WAVE; ++s) {
+            const int job = JOBS_PER_WAVE * (wave - 1) + s;
+            if (job < 2 * NBLK) {
+                const int tri = job % NBLK;
+                const int ti = tri >= 6 ? 3 : tri >= 3 ? 2 : tri >= 1 ? 1 : 0, tj = tri - blk(ti, 0);
+                if (job < NBLK) {
+                    decay_tile(sm.p, sm.beta, sm.tri.l, true, ti, tj, g, r, G[s]);
+                } else {  // Mq goes straight to the chunk factors: lane (g, r) holds row r, columns 4g ..
+                    const int t = 16 * ti + r, j0 = 16 * tj + 4 * g;
+                    const f32x4_t pv = ld4(&sm.p[t][j0]), bv = ld4(&sm.beta[j0]);
+                    f32x4_t out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = j0 + e <= t ? pv[e] * bv[e] * G[s][e] : 0.0f;
+                    *reinterpret_cast<f32x4_t*>(&F->mq[tri][r][4 * g]) = out;
+                }
+            }
+        }
     }
     __syncthreads();
 
-    // blocks 00, 10, 11 of T and Mq, 16 bytes per thread: piece = block * 64 + row * 4 + quarter
-    if (tid < 192) {
-        const int blk = tid >> 6, row = (tid >> 2) & 15, col = 4 * (tid & 3);
-        const int tr = 16 * (blk > 0) + row, tc = 16 * (blk == 2) + col;
-        *reinterpret_cast<f32x4_t*>(&F->t[blk][row][col]) = ld4(&sm.ti[tr][tc]);
-        *reinterpret_cast<f32x4_t*>(&F->mq[blk][row][col]) = ld4(&sm.mq[tr][tc]);
+    invert_block(sm.tri.l, sm.tri.ti, wave, g, r);  // T_ww
+    __syncthreads();
+    if (wave < 3) offdiag_block(sm.tri.l, sm.tri.ti, wave + 1, wave, g, r);  // T_10, T_21, T_32
+    __syncthreads();
+    if (wave < 2) offdiag_block(sm.tri.l, sm.tri.ti, wave + 2, wave, g, r);  // T_20, T_31
+    __syncthreads();
+    if (wave == 0) offdiag_block(sm.tri.l, sm.tri.ti, 3, 0, g, r);  // T_30
+    __syncthreads();
+
+    // the lower blocks of T, 16 bytes per thread and round: piece = block * 64 + row * 4 + quarter
+#pragma unroll
+    for (int m = 0; m < (NBLK * 64 + 255) / 256; ++m) {
+        const int pc = tid + 256 * m;
+        if (pc < NBLK * 64) {
+            const int bk = pc >> 6, row = (pc >> 2) & 15, col = 4 * (pc & 3);
+            const int bi = bk >= 6 ? 3 : bk >= 3 ? 2 : bk >= 1 ? 1 : 0, bj = bk - blk(bi, 0);
+            *reinterpret_cast<f32x4_t*>(&F->t[bk][row][col]) = ld4(&sm.tri.ti[16 * bi + row][16 * bj + col]);
+        }
     }
 }
 
-// The chunk factors a wave of the sequential kernel reads (loaded a chunk ahead).
+// The chunk factors wave w of the sequential kernel reads (loaded a chunk ahead; the same number of
+// loads in every wave): rows r, columns 4g .. 4g + 3 of T_wj and Mq_oj (o = 3 - w, the output tile
+// of wave w), j = 0 .. 3 (blocks past the diagonal repeat the diagonal one, unused); gp of every token
+// tile; ga of tile o; w of tile w; P(end, start).
 struct FactorRegs {
-    f32x4_t fa, fb;  // factor rows (T for waves 0, 1; Mq for waves 2, 3), columns 4g .. 4g + 3
-    f32x4_t g0, g1;  // waves 0, 1: gp at tokens 4g + e and 16 + 4g + e; waves 2, 3: ga at 16 tt + 4g + e
-    f32x4_t wt;      // w at tokens 16 tt + 4g + e
+    f32x4_t t[NTT], mq[NTT], gp[NTT];
+    f32x4_t ga, wt;
     float gend;
 };
 
-// A chunk's keys, queries and value columns as staged by waves 2 and 3 (thread i = 0 .. 127): 16-byte
-// pieces i + 128 m (token piece / 16, elements 8 (piece % 16) ..) and value elements i + 128 m (token
-// e / 16, column e % 16), m = 0 .. 3.
+// A chunk's keys, queries and value columns, staged by thread i (0 .. 255): 16-byte pieces i + 256 m
+// (token piece / 16, elements 8 (piece % 16) ..) and value elements i + 256 m (token e / 16, column
+// e % 16), m = 0 .. 3.
+constexpr int PIECES = CH * 16 / 256;
 struct PieceRegs {
-    qu32x4 k[4], q[4];
-    uint32_t v[4];
+    qu32x4 k[PIECES], q[PIECES];
+    uint32_t v[PIECES];
 };
 
 struct MainLds {
-    __bf16 k[2][CH][KP];    // keys of chunks c and c + 1
-    __bf16 q[2][CH][KP];    // queries
-    float v[2][NV][FP];     // the workgroup's value columns, value-major
-    f32x4_t red[4][4][64];  // partial K S0 (tiles 0, 1) and Q S0 (tiles 0, 1) of each wave's key rows
-    float u[NV][FP];        // U, value-major
-    __bf16 wu[3][NV][WP];   // w U split in three bf16 parts, value-major
+    __bf16 k[2][CH][KP];            // keys of chunks c and c + 1
+    __bf16 q[2][CH][KP];            // queries
+    float v[2][NV][FP];             // the workgroup's value columns, value-major
+    f32x4_t red[4][2 * NTT][64];    // partial K S0 and Q S0 tiles of each wave's key rows
+    float u[NV][FP];                // U, value-major
+    __bf16 wu[3][NV][WP];           // w U split in three bf16 parts, value-major
 };
 
 __device__ __forceinline__ void load_factors(FactorRegs& fr, const ChunkFactors* F, int wave, int g, int r,
                                              int vzero) {
-    // wave 0: T_00; wave 1: T_10, T_11; wave 2: Mq_00; wave 3: Mq_10, Mq_11
-    const float* base = wave < 2 ? &F->t[0][0][0] : &F->mq[0][0][0];
-    const int ia = wave & 1, ib = (wave & 1) ? 2 : 0;
-    fr.fa = ld4(base + ia * 256 + 16 * r + 4 * g);
-    fr.fb = ld4(base + ib * 256 + 16 * r + 4 * g);
-    const int tt = wave & 1;
-    fr.g0 = ld4((wave < 2 ? F->gp : F->ga + 16 * tt) + 4 * g);
-    fr.g1 = ld4(F->gp + 16 + 4 * g);
-    fr.wt = ld4(F->w + 16 * tt + 4 * g);
+    const int o = 3 - wave, off = 16 * r + 4 * g;
+#pragma unroll
+    for (int j = 0; j < NTT; ++j) {
+        fr.t[j] = ld4(&F->t[blk(wave, j <= wave ? j : wave)][0][0] + off);
+        fr.mq[j] = ld4(&F->mq[blk(o, j <= o ? j : o)][0][0] + off);
+        fr.gp[j] = ld4(F->gp + 16 * j + 4 * g);
+    }
+    fr.ga = ld4(F->ga + 16 * o + 4 * g);
+    fr.wt = ld4(F->w + 16 * wave + 4 * g);
     fr.gend = F->gend[vzero];  // a vector load (see the note at the token-by-token kernel)
 }
 
-// Per-thread byte offsets of a staging thread's pieces inside a chunk (the same for every chunk).
+// Per-thread byte offsets of a thread's pieces inside a chunk (the same for every chunk).
 struct PieceOffs {
-    uint32_t k[4], q[4], v[4];
+    uint32_t k[PIECES], q[PIECES], v[PIECES];
 };
 
 __device__ __forceinline__ PieceOffs piece_offsets(int64_t ldk, int64_t ldq, int64_t ldv, int i) {
     PieceOffs po;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t t = (uint32_t)((i >> 4) + 8 * m);
+    for (int m = 0; m < PIECES; ++m) {
+        const uint32_t t = (uint32_t)((i >> 4) + 16 * m);
         po.k[m] = t * (uint32_t)ldk * 2u + 16u * (uint32_t)(i & 15);
         po.q[m] = t * (uint32_t)ldq * 2u + 16u * (uint32_t)(i & 15);
         po.v[m] = t * (uint32_t)ldv * 2u + 2u * (uint32_t)(i & 15);
@@ -478,15 +528,11 @@ __device__ __forceinline__ void load_pieces(PieceRegs& pr, const PieceOffs& po, 
                                             int64_t cl, int64_t T) {
     const int64_t c0 = cl * CH;
     const int64_t nv = std::max<int64_t>(0, std::min<int64_t>(CH, T - c0));
-    constexpr int FLAGS = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kb + c0 * ldk), (short)0, (int)(nv * ldk * 2), FLAGS);
-    const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(qb + c0 * ldq), (short)0, (int)(nv * ldq * 2), FLAGS);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vb + c0 * ldv), (short)0, (int)(nv * ldv * 2), FLAGS);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb + c0 * ldk, nv * ldk * 2);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qb + c0 * ldq, nv * ldq * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb + c0 * ldv, nv * ldv * 2);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < PIECES; ++m) {
         pr.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)po.k[m], 0, 0);
         pr.q[m] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)po.q[m], 0, 0);
         pr.v[m] = __builtin_amdgcn_raw_buffer_load_b16(rv, (int)po.v[m], 0, 0);
@@ -495,8 +541,8 @@ __device__ __forceinline__ void load_pieces(PieceRegs& pr, const PieceOffs& po, 
 
 __device__ __forceinline__ void stage_pieces(MainLds& sm, int bi, const PieceRegs& pr, int i) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int pc = i + 128 * m, t = pc >> 4, col = 8 * (pc & 15);
+    for (int m = 0; m < PIECES; ++m) {
+        const int pc = i + 256 * m, t = pc >> 4, col = 8 * (pc & 15);
         *reinterpret_cast<qu32x4*>(&sm.k[bi][t][col]) = pr.k[m];
         *reinterpret_cast<qu32x4*>(&sm.q[bi][t][col]) = pr.q[m];
         sm.v[bi][pc & 15][t] = bf16_lo(pr.v[m]);
@@ -514,7 +560,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
     int64_t nch, int64_t nbh, const ChunkFactors* __restrict__ fac, float* __restrict__ o, int64_t ldo) {
     __shared__ __attribute__((aligned(16))) MainLds sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-    const int tt = wave & 1;
+    const int ot = 3 - wave;  // the output tile of this wave (its U tile is wave)
     // Workgroups are dealt to the 8 XCDs round-robin; the 8 value slices of one (sequence, head) go to
     // one XCD (its L2 then serves their shared keys, queries and chunk factors, and whole value rows):
     // workgroup i -> head 8 (i / 64) + i % 8, slice (i / 8) % 8. The grid is rounded up to 64.
@@ -536,16 +582,13 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
     float* sg = state + bh * GDN_D * GDN_D + (int64_t)(slice * NV + r) * GDN_D + 32 * wave + 4 * g;
     f32x4_t S[2] = {ld4(sg), ld4(sg + 16)};
 
-    auto valid = [&](int64_t c) { return (int)std::min<int64_t>(CH, T - c * CH); };
-    // waves 2 and 3 stage the chunks (their phase 2 is the shorter one)
+    // Every wave issues the same sequence of vector memory instructions, so that the compiler can
+    // count what is in flight and waits for a load only where its data is used.
     PieceRegs pieces;
-    const int si = tid - 128;
-    const PieceOffs po = piece_offsets(ldk, ldq, ldv, si);
-    if (wave >= 2) {
-        load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 0, T);
-        stage_pieces(sm, 0, pieces, si);
-        load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 1, T);
-    }
+    const PieceOffs po = piece_offsets(ldk, ldq, ldv, tid);
+    load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 0, T);
+    stage_pieces(sm, 0, pieces, tid);
+    load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, 1, T);
     FactorRegs nxt;
     load_factors(nxt, Fh, wave, g, r, vzero);
     __syncthreads();
@@ -554,9 +597,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
         const int bi = (int)(c & 1);
         const FactorRegs cur = nxt;
         load_factors(nxt, Fh + (c + 1 < nch ? c + 1 : c), wave, g, r, vzero);
-        const int n = valid(c);
 
-        // ---- phase 1: this wave's 32 key rows of K S0 and Q S0 for both token tiles. The matrix
+        // ---- phase 1: this wave's 32 key rows of K S0 and Q S0 for the 4 token tiles. The matrix
         // instruction's 8 k-slots of lane group g hold keys 32w + 4g + e and 32w + 16 + 4g + e, which are
         // exactly the state rows the lane holds.
         bf16x8_t B[3];
@@ -577,7 +619,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
+            for (int t2 = 0; t2 < NTT; ++t2) {
                 const __bf16* row = x == 0 ? &sm.k[bi][16 * t2 + r][32 * wave + 4 * g]
                                            : &sm.q[bi][16 * t2 + r][32 * wave + 4 * g];
                 const bf16x8_t A = as_bf16x8(*reinterpret_cast<const qu32x2*>(row),
@@ -586,70 +628,82 @@ __global__ __launch_bounds__(256) void gdn_chunk_kernel(
                 acc = mma_bf16(A, B[2], acc);
                 acc = mma_bf16(A, B[1], acc);
                 acc = mma_bf16(A, B[0], acc);
-                sm.red[wave][2 * x + t2][lane] = acc;
+                sm.red[wave][NTT * x + t2][lane] = acc;
             }
         __syncthreads();
 
-        // ---- phase 2: waves 0, 1: R and U for token tile tt (U_0 = T_00 R_0, U_1 = T_10 R_0 + T_11 R_1);
-        // waves 2, 3: P(t, start) Q S0 for token tile tt. Then the next chunk is staged (its buffer was
-        // last read before the barrier above) and the one after it loaded.
-        f32x4_t xs;
-        if (wave < 2) {
-            f32x4_t R[2];
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                if (t2 > tt) break;
-                const f32x4_t ks =
-                    ((sm.red[0][t2][lane] + sm.red[1][t2][lane]) + sm.red[2][t2][lane]) + sm.red[3][t2][lane];
-                const f32x4_t vv = ld4(&sm.v[bi][r][16 * t2 + 4 * g]);
-                R[t2] = vv - (t2 == 0 ? cur.g0 : cur.g1) * ks;
-            }
+        // ---- phase 2: U_w = sum_{j <= w} T_wj R_j with R_j = V_j - P(t-1, start) K_j S0 (each wave
+        // rebuilds the R tiles it needs); P(t, start) Q S0 of the output tile; the next chunk staged
+        // (its buffer was last read before the barrier above) and the one after it loaded; the state
+        // update's K^T operands (independent of U) read before the barrier.
+        {
             const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4_t U = mma16_f32(cur.fa, R[0], zero);
-            if (tt == 1) U = mma16_f32(cur.fb, R[1], U);
-            const int t0 = 16 * tt + 4 * g;
+            f32x4_t U = zero;
+#pragma unroll
+            for (int j = 0; j < NTT; ++j) {
+                if (j > wave) break;
+                const f32x4_t ks =
+                    ((sm.red[0][j][lane] + sm.red[1][j][lane]) + sm.red[2][j][lane]) + sm.red[3][j][lane];
+                const f32x4_t R = ld4(&sm.v[bi][r][16 * j + 4 * g]) - cur.gp[j] * ks;
+                U = mma16_f32(cur.t[j], R, U);
+            }
+            const int t0 = 16 * wave + 4 * g;
             *reinterpret_cast<f32x4_t*>(&sm.u[r][t0]) = U;
             bf16x4_t hh, mm, ll;
             split3(cur.wt * U, hh, mm, ll);
             *reinterpret_cast<bf16x4_t*>(&sm.wu[0][r][t0]) = hh;
             *reinterpret_cast<bf16x4_t*>(&sm.wu[1][r][t0]) = mm;
             *reinterpret_cast<bf16x4_t*>(&sm.wu[2][r][t0]) = ll;
-        } else {
-            const f32x4_t qs = ((sm.red[0][2 + tt][lane] + sm.red[1][2 + tt][lane]) + sm.red[2][2 + tt][lane]) +
-                               sm.red[3][2 + tt][lane];
-            xs = cur.g0 * qs;
-            // also past the end (zeros into the free buffer), so that the loads in flight are the same
-            // every iteration
-            stage_pieces(sm, bi ^ 1, pieces, si);
-            load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, c + 2, T);
         }
-        // the state update's K^T operands do not depend on this chunk's U: read them before the barrier
-        bf16x8_t KT[2];
+        const f32x4_t qs = ((sm.red[0][NTT + ot][lane] + sm.red[1][NTT + ot][lane]) + sm.red[2][NTT + ot][lane]) +
+                           sm.red[3][NTT + ot][lane];
+        const f32x4_t xs = cur.ga * qs;
+        // also past the end (zeros into the free buffer), so the loads in flight are the same every time
+        stage_pieces(sm, bi ^ 1, pieces, tid);
+        load_pieces(pieces, po, kb, ldk, qb, ldq, vb, ldv, c + 2, T);
+        bf16x8_t KT[2][2];  // [key tile][token half]
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) KT[kk][e] = sm.k[bi][8 * g + e][32 * wave + 16 * kk + r];
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) KT[kk][hf][e] = sm.k[bi][32 * hf + 8 * g + e][32 * wave + 16 * kk + r];
         __syncthreads();
 
-        // ---- phase 3: outputs (waves 2, 3) and the state update of each wave's key rows
-        if (wave >= 2) {
-            f32x4_t acc = mma16_f32(cur.fa, ld4(&sm.u[r][4 * g]), xs);
-            if (tt == 1) acc = mma16_f32(cur.fb, ld4(&sm.u[r][16 + 4 * g]), acc);
-            const int t0 = 16 * tt + 4 * g;
+        // ---- phase 3: outputs of tile ot = 3 - w (so every wave does 5 block products per chunk) and
+        // the state update of each wave's key rows
+        {
+            f32x4_t acc = xs;
+#pragma unroll
+            for (int j = 0; j < NTT; ++j) {
+                if (j > ot) break;
+                acc = mma16_f32(cur.mq[j], ld4(&sm.u[r][16 * j + 4 * g]), acc);
+            }
+            // bounds-checked stores: rows past the end of the sequence fall outside the descriptor
+            const int rows = (int)std::min<int64_t>(CH, T - c * CH);
+            const __amdgpu_buffer_rsrc_t ro = rsrc(ob + c * CH * ldo, ((int64_t)(rows - 1) * ldo + NV) * 4);
+            const int t0 = 16 * ot + 4 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (t0 + e < n) ob[(c * CH + t0 + e) * ldo + r] = acc[e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), ro,
+                                                      (int)(((t0 + e) * (uint32_t)ldo + r) * 4u), 0, 0);
         }
         {
-            const bf16x8_t W0 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[0][r][8 * g]);
-            const bf16x8_t W1 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[1][r][8 * g]);
-            const bf16x8_t W2 = *reinterpret_cast<const bf16x8_t*>(&sm.wu[2][r][8 * g]);
+            bf16x8_t W[2][3];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int x = 0; x < 3; ++x)
+                    W[hf][x] = *reinterpret_cast<const bf16x8_t*>(&sm.wu[x][r][32 * hf + 8 * g]);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 f32x4_t acc = cur.gend * S[kk];
-                acc = mma_bf16(KT[kk], W2, acc);
-                acc = mma_bf16(KT[kk], W1, acc);
-                acc = mma_bf16(KT[kk], W0, acc);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    acc = mma_bf16(KT[kk][hf], W[hf][2], acc);
+                    acc = mma_bf16(KT[kk][hf], W[hf][1], acc);
+                    acc = mma_bf16(KT[kk][hf], W[hf][0], acc);
+                }
                 S[kk] = acc;
             }
         }

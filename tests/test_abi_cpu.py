@@ -189,11 +189,11 @@ def gdn(L, q=A16, ldq=2048, k=A16, ldk=2048, v=A16, ldv=4096, a=A16, lda=32, b=A
 
 
 def test_gdn_workspace_bytes(L):
-    """The chunked form (32 tokens or more) keeps 6656 bytes of chunk factors per (sequence, value head,
-    32-token chunk); token-by-token calls and invalid shapes need none."""
+    """The chunked form (32 tokens or more) keeps 21504 bytes of chunk factors per (sequence, value
+    head, 64-token chunk); token-by-token calls and invalid shapes need none."""
     W = L.nvfp4_gdn_workspace_bytes
-    assert W(1, 32768, 32, 16, 128) == 1024 * 32 * 6656
-    assert W(2, 33, 4, 2, 128) == 2 * 4 * 2 * 6656
+    assert W(1, 32768, 32, 16, 128) == 512 * 32 * 21504
+    assert W(2, 33, 4, 2, 128) == 2 * 4 * 1 * 21504 and W(2, 65, 4, 2, 128) == 2 * 4 * 2 * 21504
     assert W(64, 1, 32, 16, 128) == 0 and W(3, 31, 4, 2, 128) == 0
     assert W(1, 64, 32, 16, 64) == 0 and W(1, 64, 30, 16, 128) == 0 and W(0, 64, 4, 2, 128) == 0
 
@@ -201,7 +201,7 @@ def test_gdn_workspace_bytes(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(state=None), 1), (dict(o=None), 1),
     (dict(D=64), 2), (dict(Hv=30), 2), (dict(T=-1), 2), (dict(ldv=4000), 2), (dict(lda=16), 2),
-    (dict(ldv=1 << 24), 2),
+    (dict(ldv=1 << 23), 2), (dict(ldo=1 << 23), 2),
     (dict(q=A16 + 8), 3), (dict(ldk=2052), 3), (dict(state=A16 + 4), 3), (dict(ws=A16 + 8), 3),
     (dict(ws_bytes=1024), 7), (dict(ws=None), 7),
 ])
