@@ -200,11 +200,15 @@ __global__ __launch_bounds__(256) void gdn_recurrence_kernel(
 //   * K S0, Q S0, K^T (w U): the FP32 operand is split into three bf16 parts x = h + m + l (each part
 //     the rounded remainder of the previous ones, so the sum carries 24 significant bits), which keeps
 //     FP32 accuracy at bf16 matrix rate;
-//   * T R, Mq U and the off-diagonal block of T (both operands FP32): v_mfma_f32_16x16x4_f32.
-// T is formed by 16-blocks: T_bb = (I + L_bb)^-1 by back substitution, T_10 = -T_11 L_10 T_00. The
-// decay products P(t, j) are running products (robust to underflow, no logarithms). Tokens past the
-// end of the sequence are padded with k = q = v = 0, alpha = 1, beta = 0, which leave the state
-// unchanged.
+//   * T R, Mq U and the off-diagonal blocks of T (both operands FP32): v_mfma_f32_16x16x4_f32.
+// T is formed by 16-blocks: T_ii = (I + L_ii)^-1 by back substitution, then level by level
+// T_ij = -T_ii sum_{j <= k < i} L_ik T_kj. The decay products P(t, j) are running products (robust to
+// underflow, no logarithms). Tokens past the end of the sequence are padded with k = q = v = 0,
+// alpha = 1, beta = 0, which leave the state unchanged.
+// Per chunk the sequential kernel has three phases separated by two barriers: (1) every wave's key
+// rows of K S0 and Q S0; (2) wave w builds R_0 .. R_w and U_w = sum_j T_wj R_j, and the next chunk is
+// staged; (3) wave w writes the outputs of token tile 3 - w (so each wave does five 16-block products
+// per chunk) and updates its key rows of S.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
