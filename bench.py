@@ -109,6 +109,8 @@ class Step:
                 a_log, dt_bias = torch.from_numpy(al).cuda(), torch.from_numpy(db).cuda()
             out = torch.empty((M, seg.n), dtype=dt, device=dev)
             self.segments.append(nv.Segment(seg.n, self.g_w[s], epi, dt, a_log, dt_bias, out))
+        need = nv.lib().nvfp4_gemm_workspace_bytes(M, case.N, K)
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         torch.cuda.synchronize()
         log(f"[setup] weights quantized, g_a = {self.g_a:.6g}, setup {time.time() - t0:.1f}s")
 
@@ -118,7 +120,7 @@ class Step:
     def gemm(self):
         wc, ws = self.w_copies[self.calls % len(self.w_copies)]
         self.calls += 1
-        nv.gemm(self.a_codes, self.a_scales, self.g_a, wc, ws, self.segments)
+        nv.gemm(self.a_codes, self.a_scales, self.g_a, wc, ws, self.segments, workspace=self.workspace)
 
 
 def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
@@ -519,7 +521,8 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gemm_gbps / PEAK_HBM_GBPS}
-    kernel = "gemm_skinny_kernel" if M <= 64 else "gemm_kernel"
+    kernel = ("gemm_skinny_kernel" if M <= 32 else "gemm_wide_kernel + gemm_wide_reduce_kernel") if M <= 64 \
+        else "gemm_kernel"
     tr = measured_traffic(kernel, case.name)
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,

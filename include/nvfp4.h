@@ -135,8 +135,10 @@ typedef struct {
  * The product of the decoded operands is accumulated in FP32 from exact FP16 products (an E2M1
  * value times an E4M3 scale is exact in FP16), then scaled once by RN32(g_a * g_w[s]).
  * M == 0 or N == 0 is a no-op; K == 0 writes the epilogue of y = 0.
- * workspace: device scratch of at least nvfp4_gemm_workspace_bytes(M, N, K) bytes (may be NULL
- * when that is 0).
+ * workspace: device scratch of at least nvfp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
+ * (may be NULL when that is 0; it is not for 32 < M <= 64, where the split-K partial sums of the
+ * decode kernel live there). Owned by the caller; its contents on entry do not matter, and calls
+ * that share one workspace must be ordered on one stream.
  * Errors: NULL, SHAPE, ALIGN, SEGMENTS, SCALE, EPILOGUE, WORKSPACE, HIP.
  */
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
@@ -145,7 +147,8 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
                         const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none). */
+/* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none): for 32 < M <= 64,
+ * splits(K) * N * 64 * 4 with splits(K) = min(8, max(1, ceil(K / 256) / 8)). */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------------------------

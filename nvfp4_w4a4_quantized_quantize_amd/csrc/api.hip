@@ -78,10 +78,8 @@ const char* nvfp4_status_string(nvfp4_status s) {
 const char* nvfp4_last_error(void) { return g_last_error; }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return 0;
+    return nvfp4::gemm_wide_workspace_bytes(M, N, K);
 }
 
 nvfp4_status nvfp4_global_scale(const void* x_bf16, int64_t rows, int64_t K, int64_t ldx, float* g_out,
@@ -171,11 +169,19 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     const size_t need = nvfp4_gemm_workspace_bytes(M, N, K);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (M == 0 || N == 0) return ok();
-    const auto launch = M <= nvfp4::SKINNY_MAX_M ? nvfp4::launch_gemm_skinny : nvfp4::launch_gemm_tiled;
-    return hip_status(launch(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
-                             static_cast<hipStream_t>(stream)),
-                      "nvfp4_gemm launch");
+    const hipStream_t st_ = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (M > nvfp4::SKINNY_MAX_M)
+        e = nvfp4::launch_gemm_tiled(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp, st_);
+    else if (M > nvfp4::SKINNY_NARROW_M)
+        e = nvfp4::launch_gemm_wide(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
+                                    workspace, st_);
+    else
+        e = nvfp4::launch_gemm_skinny(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
+                                      st_);
+    return hip_status(e, "nvfp4_gemm launch");
 }
 
 nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float* s_out,

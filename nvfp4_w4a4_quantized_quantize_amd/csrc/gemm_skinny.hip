@@ -94,32 +94,37 @@ __device__ __forceinline__ void load_full_chunk(Frags<MT, NT>& f, const uint8_t*
 }
 
 template <int MT, int NT>
-__device__ __forceinline__ void compute_chunk(const Frags<MT, NT>& f, f32x4 (&acc)[NT][MT]) {
+__device__ __forceinline__ void compute_frags(const RowFrag (&w)[NT], const RowFrag (&a)[MT], f32x4 (&acc)[NT][MT]) {
     half2_t sw[NT][2], sa[MT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        sw[t][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.w[t].s, 1.0f, false);
-        sw[t][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.w[t].s, 1.0f, true);
+        sw[t][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[t].s, 1.0f, false);
+        sw[t][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[t].s, 1.0f, true);
     }
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-        sa[u][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.a[u].s, 1.0f, false);
-        sa[u][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.a[u].s, 1.0f, true);
+        sa[u][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a[u].s, 1.0f, false);
+        sa[u][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a[u].s, 1.0f, true);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         // elements [8j, 8j + 8): dword j & 3 of piece j >> 2, block j >> 1
         half8_t wv[NT], av[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) wv[t] = dequant8(f.w[t].c[j >> 2][j & 3], sw[t][j >> 2][(j >> 1) & 1]);
+        for (int t = 0; t < NT; ++t) wv[t] = dequant8(w[t].c[j >> 2][j & 3], sw[t][j >> 2][(j >> 1) & 1]);
 #pragma unroll
-        for (int u = 0; u < MT; ++u) av[u] = dequant8(f.a[u].c[j >> 2][j & 3], sa[u][j >> 2][(j >> 1) & 1]);
+        for (int u = 0; u < MT; ++u) av[u] = dequant8(a[u].c[j >> 2][j & 3], sa[u][j >> 2][(j >> 1) & 1]);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int u = 0; u < MT; ++u)
                 acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[t], av[u], acc[t][u], 0, 0, 0);
     }
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void compute_chunk(const Frags<MT, NT>& f, f32x4 (&acc)[NT][MT]) {
+    compute_frags<MT, NT>(f.w, f.a, acc);
 }
 
 template <int MT, int NT>
@@ -240,7 +245,269 @@ int skinny_waves(int64_t K) {
     return (int)std::min<int64_t>(4, std::max<int64_t>(1, nch / 4));
 }
 
+// ---------------------------------------------------------------------------------------------------
+// 32 < M <= 64 ("wide" decode). With three or four activation tiles every weight tile of the kernel
+// above re-reads all activation rows of its K range from L2, which is then what bounds it. Here a
+// workgroup's four waves share one K range: each activation chunk (64 rows x 144 bytes) is staged
+// once in LDS (double buffered, one barrier per chunk) and feeds 128 weight rows (two 16-row tiles
+// per wave). K is split across workgroups by a count chosen from K alone; each split writes its
+// partial sums (FP32, [split][n][64 activation rows]) to the workspace, and a second kernel adds the
+// splits in order and applies the segment epilogue. Every output bit is thus the same for any N,
+// column group or segment table.
+
+constexpr int WIDE_NT = 2;                       // weight tiles of 16 rows per wave
+constexpr int WIDE_ROWS = 4 * 16 * WIDE_NT;      // weight rows per workgroup
+constexpr int WIDE_MP = 64;                      // activation rows held (M <= 64)
+constexpr int A_PITCH = CHUNK / 2 + CHUNK / 16;  // 144 bytes per staged activation row: codes, then scales
+
+// One thread's share of an activation chunk: code pieces i and i + 256 (row p / 8, bytes 16 (p % 8)),
+// and 4 scale bytes (row i / 4, bytes 4 (i % 4)).
+struct APieces {
+    u32x4 c[2];
+    uint32_t s;
+};
+
+// Chunk c (below K / 256) of the activations; rows clamped to M - 1 (their results are never stored).
+// Branch-free, so that the loads of later chunks stay in flight across the multiplication.
+__device__ __forceinline__ void load_a_full(APieces& p, const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
+                                            int64_t lda_s, int64_t M, int64_t c, int i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int pc = i + 256 * h;
+        p.c[h] = *reinterpret_cast<const u32x4*>(a_codes + std::min<int64_t>(pc >> 3, M - 1) * lda_c +
+                                                 c * (CHUNK / 2) + 16 * (pc & 7));
+    }
+    p.s = *reinterpret_cast<const uint32_t*>(a_scales + std::min<int64_t>(i >> 2, M - 1) * lda_s + c * (CHUNK / 16) +
+                                             4 * (i & 3));
+}
+
+// The chunk that crosses K: only bytes of elements below K are read, the rest is zero (a zero scale
+// byte makes a block contribute nothing).
+__device__ __forceinline__ void load_a_tail(APieces& p, const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
+                                            int64_t lda_s, int64_t M, int64_t K, int64_t c, int i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int pc = i + 256 * h;
+        const uint8_t* src = a_codes + std::min<int64_t>(pc >> 3, M - 1) * lda_c + c * (CHUNK / 2) + 16 * (pc & 7);
+        const int64_t v = K / 2 - (c * (CHUNK / 2) + 16 * (pc & 7));
+        if (v >= 16) {
+            p.c[h] = *reinterpret_cast<const u32x4*>(src);
+        } else if (v >= 8) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+            p.c[h] = u32x4{lo[0], lo[1], 0u, 0u};
+        } else {
+            p.c[h] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const uint8_t* src = a_scales + std::min<int64_t>(i >> 2, M - 1) * lda_s + c * (CHUNK / 16) + 4 * (i & 3);
+    const int64_t v = K / 16 - (c * (CHUNK / 16) + 4 * (i & 3));
+    uint32_t w = 0;
+    for (int b = 0; b < 4 && b < v; ++b) w |= (uint32_t)src[b] << (8 * b);
+    p.s = w;
+}
+
+__device__ __forceinline__ void stage_a(uint8_t (*buf)[A_PITCH], const APieces& p, int i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int pc = i + 256 * h;
+        *reinterpret_cast<u32x4*>(&buf[pc >> 3][16 * (pc & 7)]) = p.c[h];
+    }
+    *reinterpret_cast<uint32_t*>(&buf[i >> 2][CHUNK / 2 + 4 * (i & 3)]) = p.s;
+}
+
+template <int MT>
+__device__ __forceinline__ void read_a(RowFrag (&a)[MT], const uint8_t (*buf)[A_PITCH], int g, int r) {
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+        const uint8_t* row = buf[16 * u + r];
+        a[u].c[0] = *reinterpret_cast<const u32x4*>(row + 32 * g);
+        a[u].c[1] = *reinterpret_cast<const u32x4*>(row + 32 * g + 16);
+        a[u].s = *reinterpret_cast<const uint32_t*>(row + CHUNK / 2 + 4 * g);
+    }
+}
+
+constexpr int WIDE_SLOTS = 3;  // chunk c uses register and LDS slot (c - first chunk) % 3; loads run 2 chunks ahead
+
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_wide_kernel(
+    const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
+    const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
+    int64_t M, int64_t N, int64_t K, int64_t per, float* __restrict__ partial) {
+    __shared__ __attribute__((aligned(16))) uint8_t abuf[WIDE_SLOTS][WIDE_MP][A_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
+    const int64_t grp = blockIdx.x % groups;
+    const int split = (int)(blockIdx.x / groups);
+    const int64_t n0 = grp * WIDE_ROWS + wave * (16 * WIDE_NT);
+
+    // weight rows past N are clamped to the last row: their results are never stored
+    const uint8_t* wc[WIDE_NT];
+    const uint8_t* ws[WIDE_NT];
+#pragma unroll
+    for (int t = 0; t < WIDE_NT; ++t) {
+        const int64_t n = std::min<int64_t>(n0 + 16 * t + r, N - 1);
+        wc[t] = w_codes + n * ldw_c + 32 * g;
+        ws[t] = w_scales + n * ldw_s + 4 * g;
+    }
+
+    const int64_t nch = (K + CHUNK - 1) / CHUNK, nfull = K / CHUNK;
+    const int64_t c_lo = std::min<int64_t>(nch, split * per), c_hi = std::min<int64_t>(nch, c_lo + per);
+    const int64_t c_fhi = std::min(c_hi, nfull);  // full chunks of this split: [c_lo, c_fhi)
+
+    f32x4 acc[WIDE_NT][MT];
+#pragma unroll
+    for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (c_lo < c_fhi) {
+        // Chunk c: weights in wf[d], activations in abuf[d], d = (c - c_lo) % 3. At chunk c the loads of
+        // chunk c + 2 are issued (clamped to the last full chunk), the activations of chunk c + 1
+        // (loaded during chunk c - 1) are staged, so every load has two chunks of work to land. The
+        // body has no branch (a load under one is issued where its value is used, or waited for at the
+        // join): the loop runs in whole groups of 3 chunks, and a chunk at or past c_fhi (a repeat of
+        // the last one) gets zero weight scales, which adds exact zeros.
+        RowFrag wf[WIDE_SLOTS][WIDE_NT];
+        APieces ap[WIDE_SLOTS];
+        // chunk by chunk, in the loop's order, so that the loop's waits count the same loads on entry
+        const int64_t c1 = std::min(c_lo + 1, c_fhi - 1);
+        load_a_full(ap[0], a_codes, lda_c, a_scales, lda_s, M, c_lo, tid);
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], c_lo, wf[0][t]);
+        load_a_full(ap[1], a_codes, lda_c, a_scales, lda_s, M, c1, tid);
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], c1, wf[1][t]);
+        stage_a(abuf[0], ap[0], tid);
+        for (int64_t c0 = c_lo; c0 < c_fhi; c0 += WIDE_SLOTS) {
+#pragma unroll
+            for (int d = 0; d < WIDE_SLOTS; ++d) {
+                const int64_t c = c0 + d;
+                const int dn = (d + 2) % WIDE_SLOTS;
+                const int64_t cl = std::min(c + 2, c_fhi - 1);
+                load_a_full(ap[dn], a_codes, lda_c, a_scales, lda_s, M, cl, tid);
+#pragma unroll
+                for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], cl, wf[dn][t]);
+                __builtin_amdgcn_sched_barrier(0);  // issue them before waiting for chunk c
+                __syncthreads();                    // chunk c staged; every wave is done with chunk c - 1
+                RowFrag af[MT];
+                read_a<MT>(af, abuf[d], g, r);
+                const bool live = c < c_fhi;
+#pragma unroll
+                for (int t = 0; t < WIDE_NT; ++t) wf[d][t].s = live ? wf[d][t].s : 0u;
+                compute_frags<MT, WIDE_NT>(wf[d], af, acc);
+                stage_a(abuf[(d + 1) % WIDE_SLOTS], ap[(d + 1) % WIDE_SLOTS], tid);
+                // keep the next chunk's dequantization out of this one (it would wait for its loads)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    if (c_fhi < c_hi) {
+        // The chunk that crosses K (only in the last split). abuf[0] was last staged with a repeated
+        // chunk that no wave reads (the loop ends on d = 2).
+        APieces ap;
+        RowFrag wf[WIDE_NT], af[MT];
+        load_a_tail(ap, a_codes, lda_c, a_scales, lda_s, M, K, c_fhi, tid);
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, g, K, wf[t]);
+        stage_a(abuf[0], ap, tid);
+        __syncthreads();
+        read_a<MT>(af, abuf[0], g, r);
+        compute_frags<MT, WIDE_NT>(wf, af, acc);
+    }
+
+    // acc[t][u] of lane (g, r) holds y[n0 + 16t + 4g + e][16u + r]: partial[split][n][m]
+#pragma unroll
+    for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t n = n0 + 16 * t + 4 * g + e;
+            if (n < N) {
+                float* dst = partial + ((int64_t)split * N + n) * WIDE_MP;
+#pragma unroll
+                for (int u = 0; u < MT; ++u) dst[16 * u + r] = acc[t][u][e];
+            }
+        }
+}
+
+// The splits added in order, then the segment epilogue. A workgroup takes 16 output columns: thread
+// (column c = tid / 16, rows 4 (tid % 16) .. + 3) issues the loads of all S splits at once (float4,
+// a 4 KB contiguous run per split and workgroup), adds them in split order, and the sums go through
+// LDS so that the stores run along the output rows.
+template <int S>
+__global__ __launch_bounds__(256) void gemm_wide_reduce_kernel(const float* __restrict__ partial, int64_t M, int64_t N,
+                                                               const SegParams sp) {
+    __shared__ float tile[WIDE_MP][17];
+    const int tid = threadIdx.x;
+    const int64_t nb = (int64_t)blockIdx.x * 16;
+    const int cl = tid >> 4, m4 = 4 * (tid & 15);
+    const int64_t n = std::min<int64_t>(nb + cl, N - 1);
+    f32x4 p[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) p[s] = *reinterpret_cast<const f32x4*>(partial + ((int64_t)s * N + n) * WIDE_MP + m4);
+    f32x4 v = p[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += p[s];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[m4 + e][cl] = v[e];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int m = 16 * h + (tid >> 4), c = tid & 15;
+        if (m < M && nb + c < N) store_output(sp, m, nb + c, tile[m][c]);
+    }
+}
+
+template <int S>
+void launch_reduce(const float* partial, int64_t M, int64_t N, const SegParams& sp, hipStream_t stream) {
+    hipLaunchKernelGGL(gemm_wide_reduce_kernel<S>, dim3((uint32_t)((N + 15) / 16)), dim3(256), 0, stream, partial, M, N,
+                       sp);
+}
+
 }  // namespace
+
+// K split of the wide decode kernel, from K alone (so output bits do not depend on N): about eight
+// chunks of 256 per split and at most 8 splits, the chunks per split rounded up to a multiple of 3
+// (the kernel's loop runs in groups of 3), so the last split may be shorter.
+struct WideSplit {
+    int64_t per;  // chunks per split
+    int splits;
+};
+
+static WideSplit wide_split(int64_t K) {
+    const int64_t nch = (K + CHUNK - 1) / CHUNK;
+    if (nch == 0) return {0, 1};
+    const int64_t s0 = std::min<int64_t>(8, std::max<int64_t>(1, nch / 8));
+    const int64_t per = ((nch + s0 - 1) / s0 + 2) / 3 * 3;
+    return {per, (int)((nch + per - 1) / per)};
+}
+
+size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || N <= 0 || K < 0) return 0;
+    return (size_t)wide_split(K).splits * (size_t)N * WIDE_MP * sizeof(float);
+}
+
+hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                            const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                            int64_t M, int64_t N, int64_t K, const SegParams& sp, void* workspace,
+                            hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || !workspace) return hipErrorInvalidValue;
+    const WideSplit ks = wide_split(K);
+    const int splits = ks.splits;
+    const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
+    if (groups * splits > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    float* partial = static_cast<float*>(workspace);
+    const int mt = (int)((M + 15) / 16);
+    hipLaunchKernelGGL(mt == 3 ? gemm_wide_kernel<3> : gemm_wide_kernel<4>, dim3((uint32_t)(groups * splits)),
+                       dim3(256), 0, stream, a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N,
+                       K, ks.per, partial);
+    using reduce_fn = void (*)(const float*, int64_t, int64_t, const SegParams&, hipStream_t);
+    static constexpr reduce_fn reduce[8] = {launch_reduce<1>, launch_reduce<2>, launch_reduce<3>, launch_reduce<4>,
+                                            launch_reduce<5>, launch_reduce<6>, launch_reduce<7>, launch_reduce<8>};
+    reduce[splits - 1](partial, M, N, sp, stream);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,

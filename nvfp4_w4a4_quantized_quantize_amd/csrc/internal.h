@@ -32,8 +32,9 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t l
                            uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
                            hipStream_t stream);
 
-// Activation row counts up to SKINNY_MAX_M run on the skinny (decode) kernel, larger ones on the
-// tiled kernel.
+// Activation row counts up to SKINNY_NARROW_M run on the skinny (decode) kernel, up to SKINNY_MAX_M
+// on its wide variant (split K, partial sums in the workspace), larger ones on the tiled kernel.
+constexpr int64_t SKINNY_NARROW_M = 32;
 constexpr int64_t SKINNY_MAX_M = 64;
 
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
@@ -42,6 +43,13 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                               int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+// SKINNY_NARROW_M < M <= SKINNY_MAX_M; workspace holds gemm_wide_workspace_bytes(M, N, K) bytes.
+hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                            const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                            int64_t M, int64_t N, int64_t K, const SegParams& sp, void* workspace,
+                            hipStream_t stream);
+// Bytes of FP32 partial sums the wide variant keeps (0 outside its range of M).
+size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_kv_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float s, uint8_t* q,
                               int64_t ldq, hipStream_t stream);

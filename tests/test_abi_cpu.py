@@ -113,6 +113,25 @@ def test_gemm_rejects(L, kw, status):
     assert nv.last_error() != ""
 
 
+def test_gemm_workspace_bytes(L):
+    """Only the split-K decode kernel (32 < M <= 64) keeps partial sums: splits(K) * N * 64 FP32, with
+    splits(K) = min(8, max(1, ceil(K / 256) // 8)) depending on K alone."""
+    W = L.nvfp4_gemm_workspace_bytes
+    assert W(1, 17408, 5120) == W(32, 17408, 5120) == W(65, 17408, 5120) == 0
+    assert W(33, 17408, 5120) == W(64, 17408, 5120) == 2 * 17408 * 64 * 4
+    assert W(64, 5120, 17408) == 8 * 5120 * 64 * 4
+    assert W(48, 100, 16) == W(48, 100, 0) == 100 * 64 * 4
+    assert W(64, 64, 40) == W(-1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=40), 7), (dict(M=40, ws=A16, ws_bytes=64 * 64 * 4 - 1), 7),
+    (dict(M=40, ws=A16 + 4, ws_bytes=64 * 64 * 4), 3),
+])
+def test_gemm_wide_decode_workspace_rejects(L, kw, status):
+    assert g(L, **kw) == status, nv.last_error()
+
+
 def test_gemm_empty_shapes_ok_without_launch(L):
     assert g(L, M=0) == 0
     assert g(L, N=0, segs=[(0, 0, 0, 0, A16, 0, None, None)], n_segs=0) == 4  # still needs one segment

@@ -145,8 +145,10 @@ def test_output_guard_bands_and_strides():
     check_fp32(b[1:M + 1, 4:4 + N], y, T, "strided output")
 
 
-def test_k_zero_writes_zero_and_empty_shapes():
-    M, N = 5, 7
+@pytest.mark.parametrize("M", [5, 40, 70])
+def test_k_zero_writes_zero_and_empty_shapes(M):
+    """K = 0 on each kernel (skinny, split-K decode, tiled): the epilogue of y = 0."""
+    N = 7
     a = torch.empty((M, 0), dtype=torch.uint8, device=DEV)
     w = torch.empty((N, 0), dtype=torch.uint8, device=DEV)
     (out,) = nv.gemm(a, a, 1.0, w, w, [nv.Segment(N, 1.0)])

@@ -63,21 +63,41 @@ def test_skinny_wide_weight_tiles(M):
         check_bf16(out, y, T, f"M={M} N={N}")
 
 
+@pytest.mark.parametrize("M", [9, 40, 64])
 @pytest.mark.parametrize("K", [2048 + 16, 8192 + 128, 17408, 17408 + 16 * 7])
-def test_skinny_long_k_splits(K):
-    """Long K: up to 4 waves per column tile, uneven chunk counts, a partial last chunk."""
-    rng = np.random.default_rng(K)
-    M, N = 9, 70
+def test_skinny_long_k_splits(M, K):
+    """Long K: up to 4 waves per column tile (M <= 32) or up to 8 workgroup K-splits (M > 32), uneven
+    chunk counts, a partial last chunk."""
+    rng = np.random.default_rng(K + M)
+    N = 70 if M <= 32 else 200
     a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
     out = run_single(a, w, 2.0 ** -7, 3.0)
     y, T = expect(a, w, 2.0 ** -7, 3.0)
-    check_fp32(host(out), y, T, f"K={K}")
+    check_fp32(host(out), y, T, f"M={M} K={K}")
 
 
-def test_skinny_padded_strides_and_offsets():
+def test_wide_decode_workspace_contents_do_not_matter():
+    """M in (32, 64]: the split-K partial sums go to the caller's workspace. One workspace, filled with
+    NaN first, serves two calls in a row (the second with fewer rows, columns and chunks); each call
+    matches the oracle."""
+    rng = np.random.default_rng(91)
+    ws = torch.full((nv.lib().nvfp4_gemm_workspace_bytes(64, 300, 4112) // 4,), float("nan"),
+                    dtype=torch.float32, device=DEV)
+    for M, N, K in ((64, 300, 4112), (35, 130, 2064)):
+        assert nv.lib().nvfp4_gemm_workspace_bytes(M, N, K) <= ws.numel() * 4
+        a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
+        ac, as_ = upload(a)
+        wc, wsc = upload(w)
+        (out,) = nv.gemm(ac, as_, 0.5, wc, wsc, [nv.Segment(N, 2.0)], workspace=ws.view(torch.uint8))
+        y, T = expect(a, w, 0.5, 2.0)
+        check_fp32(host(out), y, T, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [23, 41])
+def test_skinny_padded_strides_and_offsets(M):
     """Inputs that are row slices of wider buffers (strides beyond the row), output with a stride."""
-    rng = np.random.default_rng(77)
-    M, N, K = 23, 130, 528
+    rng = np.random.default_rng(77 + M)
+    N, K = 130, 528
     a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
 
     def wide(x, extra16):
