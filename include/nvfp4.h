@@ -147,8 +147,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
                         const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none): for 32 < M <= 64,
- * splits(K) * N * 64 * 4 with splits(K) = min(8, max(1, ceil(K / 256) / 8)). */
+/* Bytes of device workspace nvfp4_gemm needs for this shape (0 when none). For 32 < M <= 64 with
+ * n = ceil(K / 256) chunks: s0 = min(8, max(1, n / 11)), p = ceil(n / s0) rounded up to even,
+ * splits = ceil(n / p); the size is splits * N * 64 * 4 when splits > 1, else 0. */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------------------------

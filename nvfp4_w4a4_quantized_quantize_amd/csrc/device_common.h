@@ -48,23 +48,47 @@ __device__ __forceinline__ float apply_gate(float y, int epi, float a_coef, floa
     return y;
 }
 
-// Scales acc by the segment's g_a * g_w, applies the segment's epilogue and stores output element
-// (row, col) of the fused GEMM into its segment's tensor.
-__device__ __forceinline__ void store_output(const SegParams& sp, int64_t row, int64_t col, float acc) {
-    const int s = segment_of(sp, col);
-    const int epi = sp.epilogue[s];
-    const int64_t j = col - sp.n_begin[s];
-    float a_coef = 0.0f, dtb = 0.0f;
-    if (epi == NVFP4_EPI_GDN_DECAY) {
-        a_coef = expf(sp.A_log[s][j]);
-        dtb = sp.dt_bias[s][j];
+// What the epilogue of one output column needs: its segment's tensor, stride, column in it, scale
+// RN32(g_a * g_w) and gate (with the column's gate parameters).
+struct ColumnOut {
+    uint8_t* out;
+    int64_t ldo, j;
+    float scale, a_coef, dtb;
+    int epi;
+    bool f32;
+};
+
+// Resolves column col (< N). The segments are walked with a wave-uniform index, so their fields come
+// from the kernel arguments by scalar loads; indexing them by a per-lane segment number instead
+// becomes a chain of dependent vector loads per element.
+__device__ __forceinline__ ColumnOut column_out(const SegParams& sp, int64_t col) {
+    ColumnOut c = {};
+    for (int t = 0; t < sp.n_segs; ++t) {
+        if (col >= sp.n_begin[t] && col < sp.n_end[t]) {
+            c.out = reinterpret_cast<uint8_t*>(sp.out[t]);
+            c.ldo = sp.ldo[t];
+            c.j = col - sp.n_begin[t];
+            c.scale = sp.scale[t];
+            c.epi = sp.epilogue[t];
+            c.f32 = sp.out_dtype[t] == NVFP4_OUT_F32;
+            if (c.epi == NVFP4_EPI_GDN_DECAY) {
+                c.a_coef = expf(sp.A_log[t][c.j]);
+                c.dtb = sp.dt_bias[t][c.j];
+            }
+        }
     }
-    const float y = apply_gate(acc * sp.scale[s], epi, a_coef, dtb);
-    const int64_t off = row * sp.ldo[s] + j;
-    if (sp.out_dtype[s] == NVFP4_OUT_F32)
-        reinterpret_cast<float*>(sp.out[s])[off] = y;
+    return c;
+}
+
+// Scales acc by the column's g_a * g_w, applies its segment's epilogue and stores output element
+// (row, col) of the fused GEMM into the segment's tensor.
+__device__ __forceinline__ void column_store(const ColumnOut& c, int64_t row, float acc) {
+    const float y = apply_gate(acc * c.scale, c.epi, c.a_coef, c.dtb);
+    const int64_t off = row * c.ldo + c.j;
+    if (c.f32)
+        reinterpret_cast<float*>(c.out)[off] = y;
     else
-        reinterpret_cast<__bf16*>(sp.out[s])[off] = (__bf16)y;
+        reinterpret_cast<__bf16*>(c.out)[off] = (__bf16)y;
 }
 
 }  // namespace nvfp4

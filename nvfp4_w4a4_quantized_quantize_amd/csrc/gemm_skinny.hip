@@ -211,18 +211,22 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
             for (int i = 0; i < 4; ++i) mine[((t * MT + u) * 4 + i) * 64 + lane] = acc[t][u][i];
     __syncthreads();
 
-    // acc[t][u][i] of lane l holds y[n0 + 16t + 4(l / 16) + i][16u + l % 16]
+    // acc[t][u][i] of lane l holds y[n0 + 16t + 4(l / 16) + i][16u + l % 16]. A thread keeps one
+    // column (the workgroup size is a multiple of COLS) and walks its rows.
     constexpr int COLS = 16 * NT;
     const int rows = (int)std::min<int64_t>(M, 16 * MT);
-    for (int idx = threadIdx.x; idx < rows * COLS; idx += blockDim.x) {
-        const int nl = idx % COLS, ml = idx / COLS;
-        const int64_t col = n0 + nl;
-        if (col >= N) continue;
-        const int t = nl >> 4, i = nl & 3, u = ml >> 4;
-        const int pos = ((t * MT + u) * 4 + i) * 64 + ((nl >> 2) & 3) * 16 + (ml & 15);
-        float s = red[pos];
-        for (int w = 1; w < kw; ++w) s += red[w * TILE + pos];
-        store_output(sp, ml, col, s);
+    const int nl = threadIdx.x % COLS;
+    const int64_t col = n0 + nl;
+    if (col < N) {
+        const ColumnOut co = column_out(sp, col);
+        const int t = nl >> 4, i = nl & 3;
+        for (int ml = threadIdx.x / COLS; ml < rows; ml += blockDim.x / COLS) {
+            const int u = ml >> 4;
+            const int pos = ((t * MT + u) * 4 + i) * 64 + ((nl >> 2) & 3) * 16 + (ml & 15);
+            float s = red[pos];
+            for (int w = 1; w < kw; ++w) s += red[w * TILE + pos];
+            column_store(co, ml, s);
+        }
     }
 }
 
@@ -247,101 +251,109 @@ int skinny_waves(int64_t K) {
 
 // ---------------------------------------------------------------------------------------------------
 // 32 < M <= 64 ("wide" decode). With three or four activation tiles every weight tile of the kernel
-// above re-reads all activation rows of its K range from L2, which is then what bounds it. Here a
-// workgroup's four waves share one K range: each activation chunk (64 rows x 144 bytes) is staged
-// once in LDS (double buffered, one barrier per chunk) and feeds 128 weight rows (two 16-row tiles
-// per wave). K is split across workgroups by a count chosen from K alone; each split writes its
-// partial sums (FP32, [split][n][64 activation rows]) to the workspace, and a second kernel adds the
-// splits in order and applies the segment epilogue. Every output bit is thus the same for any N,
-// column group or segment table.
+// above re-reads all activation rows of its K range and dequantizes them, which is then what bounds
+// it. Here a workgroup of 8 waves takes 128 weight rows (two 16-row tiles per wave) and one range of
+// K: its two "K-groups" of 4 waves take alternate 256-element chunks of that range, so each SIMD holds
+// two waves (one's dequantization overlaps the other's matrix instructions) and twice the loads are
+// in flight. Within a K-group each activation chunk is dequantized once, by the group's 256 threads,
+// into LDS as FP16 in the matrix instruction's operand order (wave u converts activation tile u, each
+// lane the 64 elements it would hold itself), and all four waves read their B operands from there;
+// a wave dequantizes only its own weight rows. Loads run two chunks ahead. The K-groups' sums are
+// added in LDS (group 0 + group 1). K is split across workgroups by a count chosen from K alone: with
+// one split the workgroup applies the segment epilogue itself, else it writes its partial sums (FP32,
+// [split][n][64 activation rows]) to the workspace and a second kernel adds the splits in order and
+// applies the epilogue. Every output bit is thus the same for any N, column group or segment table.
 
-constexpr int WIDE_NT = 2;                       // weight tiles of 16 rows per wave
-constexpr int WIDE_ROWS = 4 * 16 * WIDE_NT;      // weight rows per workgroup
-constexpr int WIDE_MP = 64;                      // activation rows held (M <= 64)
-constexpr int A_PITCH = CHUNK / 2 + CHUNK / 16;  // 144 bytes per staged activation row: codes, then scales
+constexpr int WIDE_NT = 2;                   // weight tiles of 16 rows per wave
+constexpr int WIDE_ROWS = 4 * 16 * WIDE_NT;  // weight rows per workgroup
+constexpr int WIDE_MP = 64;                  // activation rows held (M <= 64)
+constexpr int WIDE_SLOTS = 3;                // register ring: K-group chunk i in slot i % 3, loads 2 chunks ahead
+constexpr int WIDE_KG = 2;                   // K-groups of 4 waves per workgroup
 
-// One thread's share of an activation chunk: code pieces i and i + 256 (row p / 8, bytes 16 (p % 8)),
-// and 4 scale bytes (row i / 4, bytes 4 (i % 4)).
-struct APieces {
-    u32x4 c[2];
-    uint32_t s;
-};
+// One K-group's FP16 activation chunk: [tile u][step j][lane] -> the 8 values lane (g, r) feeds at
+// step j for activation row 16u + r (elements 64g + 8j .. + 7 of the chunk).
+typedef half8_t ActChunk[4][8][64];
 
-// Chunk c (below K / 256) of the activations; rows clamped to M - 1 (their results are never stored).
-// Branch-free, so that the loads of later chunks stay in flight across the multiplication.
-__device__ __forceinline__ void load_a_full(APieces& p, const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
-                                            int64_t lda_s, int64_t M, int64_t c, int i) {
+// Lane (g, r) of wave u converts its fragment of activation row 16u + r into the chunk.
+__device__ __forceinline__ void stage_act(ActChunk& dst, const RowFrag& f, int u, int lane) {
+    half2_t sa[2];
+    sa[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    sa[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int pc = i + 256 * h;
-        p.c[h] = *reinterpret_cast<const u32x4*>(a_codes + std::min<int64_t>(pc >> 3, M - 1) * lda_c +
-                                                 c * (CHUNK / 2) + 16 * (pc & 7));
-    }
-    p.s = *reinterpret_cast<const uint32_t*>(a_scales + std::min<int64_t>(i >> 2, M - 1) * lda_s + c * (CHUNK / 16) +
-                                             4 * (i & 3));
+    for (int j = 0; j < 8; ++j) dst[u][j][lane] = dequant8(f.c[j >> 2][j & 3], sa[j >> 2][(j >> 1) & 1]);
 }
 
-// The chunk that crosses K: only bytes of elements below K are read, the rest is zero (a zero scale
-// byte makes a block contribute nothing).
-__device__ __forceinline__ void load_a_tail(APieces& p, const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
-                                            int64_t lda_s, int64_t M, int64_t K, int64_t c, int i) {
+// The MT x WIDE_NT tiles of one chunk: weights dequantized here, activations read from the chunk.
+template <int MT>
+__device__ __forceinline__ void compute_lds(const RowFrag (&w)[WIDE_NT], const ActChunk& act, int lane,
+                                            f32x4 (&acc)[WIDE_NT][MT]) {
+    half2_t sw[WIDE_NT][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int pc = i + 256 * h;
-        const uint8_t* src = a_codes + std::min<int64_t>(pc >> 3, M - 1) * lda_c + c * (CHUNK / 2) + 16 * (pc & 7);
-        const int64_t v = K / 2 - (c * (CHUNK / 2) + 16 * (pc & 7));
-        if (v >= 16) {
-            p.c[h] = *reinterpret_cast<const u32x4*>(src);
-        } else if (v >= 8) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-            p.c[h] = u32x4{lo[0], lo[1], 0u, 0u};
-        } else {
-            p.c[h] = u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int t = 0; t < WIDE_NT; ++t) {
+        sw[t][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[t].s, 1.0f, false);
+        sw[t][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[t].s, 1.0f, true);
     }
-    const uint8_t* src = a_scales + std::min<int64_t>(i >> 2, M - 1) * lda_s + c * (CHUNK / 16) + 4 * (i & 3);
-    const int64_t v = K / 16 - (c * (CHUNK / 16) + 4 * (i & 3));
-    uint32_t w = 0;
-    for (int b = 0; b < 4 && b < v; ++b) w |= (uint32_t)src[b] << (8 * b);
-    p.s = w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        half8_t wv[WIDE_NT], av[MT];
+#pragma unroll
+        for (int u = 0; u < MT; ++u) av[u] = act[u][j][lane];
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t) wv[t] = dequant8(w[t].c[j >> 2][j & 3], sw[t][j >> 2][(j >> 1) & 1]);
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+            for (int u = 0; u < MT; ++u)
+                acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[t], av[u], acc[t][u], 0, 0, 0);
+    }
 }
 
-__device__ __forceinline__ void stage_a(uint8_t (*buf)[A_PITCH], const APieces& p, int i) {
+// One K-group's step i (register slot d = i % 3, LDS buffer i % 2): issue the loads of its chunk
+// i + 2 (clamped to the last full chunk), wait for chunk i (converted into act[i % 2]), multiply it,
+// convert the activations of chunk i + 1 into the other buffer. A chunk index at or past c_fhi (a
+// repeat of the last full chunk) gets zero weight scales, which adds exact zeros. There is no branch
+// in here: a load under one is issued where its value is used, or waited for at the join.
+template <int MT, bool LOADS>
+__device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c_fhi, int64_t cl,
+                                          RowFrag (&wf)[WIDE_SLOTS][WIDE_NT], RowFrag (&af)[WIDE_SLOTS],
+                                          ActChunk* act, f32x4 (&acc)[WIDE_NT][MT], const uint8_t* ac,
+                                          const uint8_t* as, const uint8_t* const (&wc)[WIDE_NT],
+                                          const uint8_t* const (&ws)[WIDE_NT], int u, int lane) {
+    const int dn = (d + 2) % WIDE_SLOTS;
+    if constexpr (LOADS) {
+        load_full(ac, as, cl, af[dn]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int pc = i + 256 * h;
-        *reinterpret_cast<u32x4*>(&buf[pc >> 3][16 * (pc & 7)]) = p.c[h];
+        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], cl, wf[dn][t]);
     }
-    *reinterpret_cast<uint32_t*>(&buf[i >> 2][CHUNK / 2 + 4 * (i & 3)]) = p.s;
+    __builtin_amdgcn_sched_barrier(0);  // issue them before waiting for chunk c
+    __syncthreads();                    // chunk c converted; every wave is done with the other buffer
+    const bool live = c < c_fhi;
+#pragma unroll
+    for (int t = 0; t < WIDE_NT; ++t) wf[d][t].s = live ? wf[d][t].s : 0u;
+    compute_lds<MT>(wf[d], act[i & 1], lane, acc);
+    stage_act(act[(i + 1) & 1], af[(d + 1) % WIDE_SLOTS], u, lane);
+    // keep the next chunk's dequantization out of this one (it would wait for its loads)
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int MT>
-__device__ __forceinline__ void read_a(RowFrag (&a)[MT], const uint8_t (*buf)[A_PITCH], int g, int r) {
-#pragma unroll
-    for (int u = 0; u < MT; ++u) {
-        const uint8_t* row = buf[16 * u + r];
-        a[u].c[0] = *reinterpret_cast<const u32x4*>(row + 32 * g);
-        a[u].c[1] = *reinterpret_cast<const u32x4*>(row + 32 * g + 16);
-        a[u].s = *reinterpret_cast<const uint32_t*>(row + CHUNK / 2 + 4 * g);
-    }
-}
-
-constexpr int WIDE_SLOTS = 3;  // chunk c uses register and LDS slot (c - first chunk) % 3; loads run 2 chunks ahead
-
-template <int MT>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(
+__global__ __launch_bounds__(512) void gemm_wide_kernel(
     const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
     const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
-    int64_t M, int64_t N, int64_t K, int64_t per, float* __restrict__ partial) {
-    __shared__ __attribute__((aligned(16))) uint8_t abuf[WIDE_SLOTS][WIDE_MP][A_PITCH];
+    int64_t M, int64_t N, int64_t K, int64_t per, float* __restrict__ partial, const SegParams sp) {
+    // two FP16 activation buffers per K-group (128 KB); reused at the end for the cross-group sum and
+    // the output tile
+    __shared__ ActChunk lds[WIDE_KG][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = wave >> 2, u = wave & 3;
     const int r = lane & 15, g = lane >> 4;
     const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
     const int64_t grp = blockIdx.x % groups;
     const int split = (int)(blockIdx.x / groups);
-    const int64_t n0 = grp * WIDE_ROWS + wave * (16 * WIDE_NT);
+    const int64_t n0 = grp * WIDE_ROWS + u * (16 * WIDE_NT);
 
-    // weight rows past N are clamped to the last row: their results are never stored
+    // weight rows past N and activation rows past M are clamped to the last row: their results are
+    // never stored
     const uint8_t* wc[WIDE_NT];
     const uint8_t* ws[WIDE_NT];
 #pragma unroll
@@ -350,84 +362,120 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(
         wc[t] = w_codes + n * ldw_c + 32 * g;
         ws[t] = w_scales + n * ldw_s + 4 * g;
     }
+    const int64_t arow = std::min<int64_t>(16 * u + r, M - 1);
+    const uint8_t* ac = a_codes + arow * lda_c + 32 * g;
+    const uint8_t* as = a_scales + arow * lda_s + 4 * g;
 
     const int64_t nch = (K + CHUNK - 1) / CHUNK, nfull = K / CHUNK;
     const int64_t c_lo = std::min<int64_t>(nch, split * per), c_hi = std::min<int64_t>(nch, c_lo + per);
     const int64_t c_fhi = std::min(c_hi, nfull);  // full chunks of this split: [c_lo, c_fhi)
+    // K-group kg takes the full chunks c_lo + 2i + kg, i < steps
+    const int64_t steps = (c_fhi - c_lo + 1) / 2;
+    auto chunk = [&](int64_t i) { return c_lo + 2 * i + kg; };
+    auto clamped = [&](int64_t i) { return std::min(chunk(i), c_fhi - 1); };
 
     f32x4 acc[WIDE_NT][MT];
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t)
 #pragma unroll
-        for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int uu = 0; uu < MT; ++uu) acc[t][uu] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (c_lo < c_fhi) {
-        // Chunk c: weights in wf[d], activations in abuf[d], d = (c - c_lo) % 3. At chunk c the loads of
-        // chunk c + 2 are issued (clamped to the last full chunk), the activations of chunk c + 1
-        // (loaded during chunk c - 1) are staged, so every load has two chunks of work to land. The
-        // body has no branch (a load under one is issued where its value is used, or waited for at the
-        // join): the loop runs in whole groups of 3 chunks, and a chunk at or past c_fhi (a repeat of
-        // the last one) gets zero weight scales, which adds exact zeros.
-        RowFrag wf[WIDE_SLOTS][WIDE_NT];
-        APieces ap[WIDE_SLOTS];
-        // chunk by chunk, in the loop's order, so that the loop's waits count the same loads on entry
-        const int64_t c1 = std::min(c_lo + 1, c_fhi - 1);
-        load_a_full(ap[0], a_codes, lda_c, a_scales, lda_s, M, c_lo, tid);
+    ActChunk* act = lds[kg];
+    if (steps > 0) {
+        RowFrag wf[WIDE_SLOTS][WIDE_NT], af[WIDE_SLOTS];
+        // step by step, in the loop's order, so that the loop's waits count the same loads on entry
+        load_full(ac, as, clamped(0), af[0]);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], c_lo, wf[0][t]);
-        load_a_full(ap[1], a_codes, lda_c, a_scales, lda_s, M, c1, tid);
+        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], clamped(0), wf[0][t]);
+        load_full(ac, as, clamped(1), af[1]);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], c1, wf[1][t]);
-        stage_a(abuf[0], ap[0], tid);
-        for (int64_t c0 = c_lo; c0 < c_fhi; c0 += WIDE_SLOTS) {
+        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], clamped(1), wf[1][t]);
+        stage_act(act[0], af[0], u, lane);
+        int64_t i0 = 0;
+        for (; i0 + WIDE_SLOTS <= steps; i0 += WIDE_SLOTS) {
 #pragma unroll
-            for (int d = 0; d < WIDE_SLOTS; ++d) {
-                const int64_t c = c0 + d;
-                const int dn = (d + 2) % WIDE_SLOTS;
-                const int64_t cl = std::min(c + 2, c_fhi - 1);
-                load_a_full(ap[dn], a_codes, lda_c, a_scales, lda_s, M, cl, tid);
-#pragma unroll
-                for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], cl, wf[dn][t]);
-                __builtin_amdgcn_sched_barrier(0);  // issue them before waiting for chunk c
-                __syncthreads();                    // chunk c staged; every wave is done with chunk c - 1
-                RowFrag af[MT];
-                read_a<MT>(af, abuf[d], g, r);
-                const bool live = c < c_fhi;
-#pragma unroll
-                for (int t = 0; t < WIDE_NT; ++t) wf[d][t].s = live ? wf[d][t].s : 0u;
-                compute_frags<MT, WIDE_NT>(wf[d], af, acc);
-                stage_a(abuf[(d + 1) % WIDE_SLOTS], ap[(d + 1) % WIDE_SLOTS], tid);
-                // keep the next chunk's dequantization out of this one (it would wait for its loads)
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int d = 0; d < WIDE_SLOTS; ++d)
+                wide_step<MT, true>(d, i0 + d, chunk(i0 + d), c_fhi, clamped(i0 + d + 2), wf, af, act, acc, ac, as,
+                                    wc, ws, u, lane);
         }
+        // the last one or two steps: their chunks are already loaded (slots 0 and 1)
+        if (i0 < steps)
+            wide_step<MT, false>(0, i0, chunk(i0), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
+        if (i0 + 1 < steps)
+            wide_step<MT, false>(1, i0 + 1, chunk(i0 + 1), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
     }
     if (c_fhi < c_hi) {
-        // The chunk that crosses K (only in the last split). abuf[0] was last staged with a repeated
-        // chunk that no wave reads (the loop ends on d = 2).
-        APieces ap;
-        RowFrag wf[WIDE_NT], af[MT];
-        load_a_tail(ap, a_codes, lda_c, a_scales, lda_s, M, K, c_fhi, tid);
+        // the chunk that crosses K (only in the last split), multiplied by K-group 0
+        __syncthreads();  // every wave is done with the activation buffers
+        RowFrag twf[WIDE_NT];
+        if (kg == 0) {
+            RowFrag taf;
+            load_tail(ac, as, c_fhi, g, K, taf);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, g, K, wf[t]);
-        stage_a(abuf[0], ap, tid);
+            for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, g, K, twf[t]);
+            stage_act(act[0], taf, u, lane);
+        }
         __syncthreads();
-        read_a<MT>(af, abuf[0], g, r);
-        compute_frags<MT, WIDE_NT>(wf, af, acc);
+        if (kg == 0) compute_lds<MT>(twf, act[0], lane, acc);
     }
 
-    // acc[t][u] of lane (g, r) holds y[n0 + 16t + 4g + e][16u + r]: partial[split][n][m]
+    // K-group 0 + K-group 1, through LDS. acc[t][uu] of lane (g, r) holds y[n0 + 16t + 4g + e][16uu + r].
+    constexpr int ACC = WIDE_NT * MT * 4;
+    float* red = reinterpret_cast<float*>(&lds[0][0][0][0][0]);
+    __syncthreads();  // every wave is done with the activation buffers
+    if (kg == 1) {
 #pragma unroll
-    for (int t = 0; t < WIDE_NT; ++t)
+        for (int t = 0; t < WIDE_NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t n = n0 + 16 * t + 4 * g + e;
-            if (n < N) {
-                float* dst = partial + ((int64_t)split * N + n) * WIDE_MP;
+            for (int uu = 0; uu < MT; ++uu)
 #pragma unroll
-                for (int u = 0; u < MT; ++u) dst[16 * u + r] = acc[t][u][e];
-            }
+                for (int e = 0; e < 4; ++e) red[(u * ACC + (t * MT + uu) * 4 + e) * 64 + lane] = acc[t][uu][e];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+            for (int uu = 0; uu < MT; ++uu)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[t][uu][e] += red[(u * ACC + (t * MT + uu) * 4 + e) * 64 + lane];
+    }
+
+    if (gridDim.x == groups) {
+        // one split: the epilogue here, through an LDS tile [m][column] so that stores run along rows
+        float(*tile)[WIDE_ROWS + 1] = reinterpret_cast<float(*)[WIDE_ROWS + 1]>(&lds[0][0][0][0][0]);
+        __syncthreads();  // the group sums are read
+        if (kg == 0) {
+#pragma unroll
+            for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+                for (int uu = 0; uu < MT; ++uu)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tile[16 * uu + r][u * 32 + 16 * t + 4 * g + e] = acc[t][uu][e];
         }
+        __syncthreads();
+        // a thread keeps one column and walks every fourth row
+        const int rows = (int)std::min<int64_t>(M, 16 * MT);
+        const int nl = tid % WIDE_ROWS;
+        const int64_t n = grp * WIDE_ROWS + nl;
+        if (n < N) {
+            const ColumnOut co = column_out(sp, n);
+            for (int m = tid / WIDE_ROWS; m < rows; m += 512 / WIDE_ROWS) column_store(co, m, tile[m][nl]);
+        }
+    } else if (kg == 0) {
+        // partial[split][n][m]
+#pragma unroll
+        for (int t = 0; t < WIDE_NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t n = n0 + 16 * t + 4 * g + e;
+                if (n < N) {
+                    float* dst = partial + ((int64_t)split * N + n) * WIDE_MP;
+#pragma unroll
+                    for (int uu = 0; uu < MT; ++uu) dst[16 * uu + r] = acc[t][uu][e];
+                }
+            }
+    }
 }
 
 // The splits added in order, then the segment epilogue. A workgroup takes 16 output columns: thread
@@ -451,10 +499,14 @@ __global__ __launch_bounds__(256) void gemm_wide_reduce_kernel(const float* __re
 #pragma unroll
     for (int e = 0; e < 4; ++e) tile[m4 + e][cl] = v[e];
     __syncthreads();
+    const int c = tid & 15;
+    if (nb + c < N) {
+        const ColumnOut co = column_out(sp, nb + c);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const int m = 16 * h + (tid >> 4), c = tid & 15;
-        if (m < M && nb + c < N) store_output(sp, m, nb + c, tile[m][c]);
+        for (int h = 0; h < 4; ++h) {
+            const int m = 16 * h + (tid >> 4);
+            if (m < M) column_store(co, m, tile[m][c]);
+        }
     }
 }
 
@@ -466,9 +518,10 @@ void launch_reduce(const float* partial, int64_t M, int64_t N, const SegParams& 
 
 }  // namespace
 
-// K split of the wide decode kernel, from K alone (so output bits do not depend on N): about eight
-// chunks of 256 per split and at most 8 splits, the chunks per split rounded up to a multiple of 3
-// (the kernel's loop runs in groups of 3), so the last split may be shorter.
+// K split of the wide decode kernel, from K alone (so output bits do not depend on N): at least 11
+// chunks of 256 per split, at most 8 splits, an even number of chunks per split (the two K-groups
+// take alternate chunks), so the last split may be shorter. A workgroup holds a whole CU (8 waves of
+// about 200 registers), so more splits than the CUs take pay a second round of workgroups.
 struct WideSplit {
     int64_t per;  // chunks per split
     int splits;
@@ -477,14 +530,15 @@ struct WideSplit {
 static WideSplit wide_split(int64_t K) {
     const int64_t nch = (K + CHUNK - 1) / CHUNK;
     if (nch == 0) return {0, 1};
-    const int64_t s0 = std::min<int64_t>(8, std::max<int64_t>(1, nch / 8));
-    const int64_t per = ((nch + s0 - 1) / s0 + 2) / 3 * 3;
+    const int64_t s0 = std::min<int64_t>(8, std::max<int64_t>(1, nch / 11));
+    const int64_t per = ((nch + s0 - 1) / s0 + 1) / 2 * 2;
     return {per, (int)((nch + per - 1) / per)};
 }
 
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || N <= 0 || K < 0) return 0;
-    return (size_t)wide_split(K).splits * (size_t)N * WIDE_MP * sizeof(float);
+    const int splits = wide_split(K).splits;
+    return splits > 1 ? (size_t)splits * (size_t)N * WIDE_MP * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
@@ -492,20 +546,22 @@ hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t
                             int64_t M, int64_t N, int64_t K, const SegParams& sp, void* workspace,
                             hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || !workspace) return hipErrorInvalidValue;
     const WideSplit ks = wide_split(K);
-    const int splits = ks.splits;
+    if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || (ks.splits > 1 && !workspace)) return hipErrorInvalidValue;
     const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
-    if (groups * splits > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    if (groups * ks.splits > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     float* partial = static_cast<float*>(workspace);
     const int mt = (int)((M + 15) / 16);
-    hipLaunchKernelGGL(mt == 3 ? gemm_wide_kernel<3> : gemm_wide_kernel<4>, dim3((uint32_t)(groups * splits)),
-                       dim3(256), 0, stream, a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N,
-                       K, ks.per, partial);
-    using reduce_fn = void (*)(const float*, int64_t, int64_t, const SegParams&, hipStream_t);
-    static constexpr reduce_fn reduce[8] = {launch_reduce<1>, launch_reduce<2>, launch_reduce<3>, launch_reduce<4>,
-                                            launch_reduce<5>, launch_reduce<6>, launch_reduce<7>, launch_reduce<8>};
-    reduce[splits - 1](partial, M, N, sp, stream);
+    hipLaunchKernelGGL(mt == 3 ? gemm_wide_kernel<3> : gemm_wide_kernel<4>, dim3((uint32_t)(groups * ks.splits)),
+                       dim3(512), 0, stream, a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N,
+                       K, ks.per, partial, sp);
+    if (ks.splits > 1) {
+        using reduce_fn = void (*)(const float*, int64_t, int64_t, const SegParams&, hipStream_t);
+        static constexpr reduce_fn reduce[8] = {launch_reduce<1>, launch_reduce<2>, launch_reduce<3>,
+                                                launch_reduce<4>, launch_reduce<5>, launch_reduce<6>,
+                                                launch_reduce<7>, launch_reduce<8>};
+        reduce[ks.splits - 1](partial, M, N, sp, stream);
+    }
     return hipGetLastError();
 }
 

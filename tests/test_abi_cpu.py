@@ -113,22 +113,39 @@ def test_gemm_rejects(L, kw, status):
     assert nv.last_error() != ""
 
 
+def wide_splits(K):
+    """The split-K count of the decode kernel for 32 < M <= 64, as its header states: n = ceil(K / 256)
+    chunks, s0 = min(8, max(1, n // 11)), chunks per split p = ceil(n / s0) rounded up to even, splits
+    ceil(n / p); from K alone."""
+    n = -(-K // 256)
+    if n == 0:
+        return 1
+    s0 = min(8, max(1, n // 11))
+    p = (-(-n // s0) + 1) // 2 * 2
+    return -(-n // p)
+
+
 def test_gemm_workspace_bytes(L):
-    """Only the split-K decode kernel (32 < M <= 64) keeps partial sums: splits(K) * N * 64 FP32, with
-    splits(K) = min(8, max(1, ceil(K / 256) // 8)) depending on K alone."""
+    """Only the split-K decode kernel (32 < M <= 64, more than one split) keeps partial sums:
+    splits * N * 64 FP32."""
     W = L.nvfp4_gemm_workspace_bytes
-    assert W(1, 17408, 5120) == W(32, 17408, 5120) == W(65, 17408, 5120) == 0
-    assert W(33, 17408, 5120) == W(64, 17408, 5120) == 2 * 17408 * 64 * 4
-    assert W(64, 5120, 17408) == 8 * 5120 * 64 * 4
-    assert W(48, 100, 16) == W(48, 100, 0) == 100 * 64 * 4
+    assert [wide_splits(K) for K in (0, 16, 5120, 5632, 8320, 17408, 17520, 1 << 20)] == [1, 1, 1, 2, 3, 6, 6, 8]
+    assert W(1, 5120, 17408) == W(32, 5120, 17408) == W(65, 5120, 17408) == 0
+    assert W(33, 5120, 17408) == W(64, 5120, 17408) == 6 * 5120 * 64 * 4
+    assert W(64, 17408, 5120) == W(48, 100, 16) == W(48, 100, 0) == 0
+    assert W(40, 300, 8320) == 3 * 300 * 64 * 4
     assert W(64, 64, 40) == W(-1, 64, 64) == 0
 
 
+WIDE = dict(M=40, K=5632, lda_c=2816, lda_s=352, ldw_c=2816, ldw_s=352)  # two K splits, N = 64
+
+
 @pytest.mark.parametrize("kw,status", [
-    (dict(M=40), 7), (dict(M=40, ws=A16, ws_bytes=64 * 64 * 4 - 1), 7),
-    (dict(M=40, ws=A16 + 4, ws_bytes=64 * 64 * 4), 3),
+    (dict(WIDE), 7), (dict(WIDE, ws=A16, ws_bytes=2 * 64 * 64 * 4 - 1), 7),
+    (dict(WIDE, ws=A16 + 4, ws_bytes=2 * 64 * 64 * 4), 3),
 ])
 def test_gemm_wide_decode_workspace_rejects(L, kw, status):
+    assert L.nvfp4_gemm_workspace_bytes(40, 64, 5632) == 2 * 64 * 64 * 4
     assert g(L, **kw) == status, nv.last_error()
 
 

@@ -77,13 +77,14 @@ def test_skinny_long_k_splits(M, K):
 
 
 def test_wide_decode_workspace_contents_do_not_matter():
-    """M in (32, 64]: the split-K partial sums go to the caller's workspace. One workspace, filled with
-    NaN first, serves two calls in a row (the second with fewer rows, columns and chunks); each call
-    matches the oracle."""
+    """M in (32, 64] with K long enough for two K splits: the partial sums go to the caller's workspace.
+    One workspace, filled with NaN first, serves two calls in a row (the second with fewer rows,
+    columns and chunks); each call matches the oracle."""
     rng = np.random.default_rng(91)
-    ws = torch.full((nv.lib().nvfp4_gemm_workspace_bytes(64, 300, 4112) // 4,), float("nan"),
+    ws = torch.full((nv.lib().nvfp4_gemm_workspace_bytes(64, 300, 8320) // 4,), float("nan"),
                     dtype=torch.float32, device=DEV)
-    for M, N, K in ((64, 300, 4112), (35, 130, 2064)):
+    assert ws.numel() > 0
+    for M, N, K in ((64, 300, 8320), (35, 130, 6160)):
         assert nv.lib().nvfp4_gemm_workspace_bytes(M, N, K) <= ws.numel() * 4
         a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
         ac, as_ = upload(a)
