@@ -1,4 +1,5 @@
-// Skinny block-scaled W4A4 GEMM for decode (M <= 64 activation rows), for gfx950 (CDNA4).
+// Block-scaled W4A4 GEMMs for decode (M <= 64 activation rows), for gfx950 (CDNA4): the skinny
+// kernel for M <= 32 and the wide kernel (further down) for 32 < M <= 64.
 //
 //   y[m, n] = g_a * g_w[seg(n)] * sum_k e2m1(qa[m,k]) sa[m,k/16] * e2m1(qw[n,k]) sw[n,k/16]
 //
@@ -21,7 +22,7 @@
 //  * v_mfma_f32_16x16x32_f16 with 16 weight rows as the rows of A and 16 activation rows as the
 //    columns of B; at step j (0..7) each lane feeds its elements [8j, 8j + 8). Both operands are
 //    dequantized to FP16 exactly (see dequant8), products are exact in FP32 and accumulate in FP32.
-//    MT = ceil(M / 16) activation tiles and NT weight tiles per wave.
+//    MT = ceil(M / 16) activation tiles and NT weight tiles per wave (1 for M <= 4, else 2).
 //  * The loads of the next DEPTH chunks are in flight while a chunk is dequantized and multiplied.
 //  * The KW partial sums meet in LDS and are added in wave order (deterministic), then scaled by
 //    g_a * g_w of the column's segment, gated and stored, consecutive threads on consecutive columns.
@@ -233,13 +234,9 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
 typedef void (*skinny_fn)(const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*,
                           int64_t, int64_t, int64_t, int64_t, const SegParams);
 
-// NT = 4 only for MT <= 2: with more activation tiles the operands no longer fit in registers.
 template <int MT>
 skinny_fn pick_nt(int nt) {
-    if constexpr (MT <= 2)
-        if (nt >= 4) return gemm_skinny_kernel<MT, 4>;
-    if (nt >= 2) return gemm_skinny_kernel<MT, 2>;
-    return gemm_skinny_kernel<MT, 1>;
+    return nt >= 2 ? gemm_skinny_kernel<MT, 2> : gemm_skinny_kernel<MT, 1>;
 }
 
 // Waves per workgroup splitting K: depends on K alone, so the order of the additions (and so every
@@ -571,10 +568,11 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8
     if (M == 0 || N == 0) return hipSuccess;
     if (M > SKINNY_MAX_M) return hipErrorInvalidValue;
     const int mt = (int)((M + 15) / 16);
-    // widest weight tile that still leaves two workgroups per compute unit
-    int nt = 1;
-    while (nt < 4 && (N + 32 * nt - 1) / (32 * nt) >= 512) nt *= 2;
-    if (mt >= 3) nt = std::min(nt, 2);
+    // Two weight tiles per wave share each activation fragment; with one or a few activation rows
+    // those loads are cheap and one tile per wave (twice the workgroups) streams the weights faster.
+    // Measured on the MLP and GDN projection shapes (N = 5120 .. 17408, K = 5120 .. 17408); N only
+    // decides how columns are grouped, never the order of any sum.
+    const int nt = M <= 4 ? 1 : 2;
     const skinny_fn fn = mt == 1   ? pick_nt<1>(nt)
                          : mt == 2 ? pick_nt<2>(nt)
                          : mt == 3 ? pick_nt<3>(nt)

@@ -1,11 +1,12 @@
 """GPU parity of the decode (M <= 64) GEMM path against the oracle.
 
-Activation row counts up to 64 run on the skinny kernel: these tests cover every activation-tile
-count (M = 1 .. 64, ragged), every weight-tile width the launcher picks (N large enough for 2 and 4
-tiles of 16 rows per wave), K-splits over 1 .. 4 waves with ragged chunk counts and a ragged final
-chunk, padded input strides, multi-segment tables with gate epilogues, bitwise agreement of a fused
-call with the same modules called one by one, repeatability, and the switch to the tiled kernel at
-M = 65. Acceptance is the bound stated in gpu_common.
+Activation row counts up to 32 run on the skinny kernel, 33 .. 64 on the wide (split-K) kernel:
+these tests cover every activation-tile count (M = 1 .. 64, ragged), both weight-tile widths of the
+skinny kernel (1 tile per wave for M <= 4, 2 above) at large N, K-splits over 1 .. 4 waves and over
+1 .. 8 workgroups with ragged chunk counts and a ragged final chunk, padded input strides, a reused
+workspace, multi-segment tables with gate epilogues, bitwise agreement of a fused call with the same
+modules called one by one, repeatability, and the switch to the tiled kernel at M = 65. Acceptance
+is the bound stated in gpu_common.
 """
 import numpy as np
 import pytest
@@ -52,9 +53,9 @@ def test_skinny_random_codes(M, N, K):
     check_fp32(host(out), y, T, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 20, 40, 64])
+@pytest.mark.parametrize("M", [1, 4, 5, 20, 40, 64])
 def test_skinny_wide_weight_tiles(M):
-    """N large enough that the launcher takes 2 or 4 weight tiles of 16 rows per wave."""
+    """Large N, with one weight tile per wave (M <= 4) and two (M > 4), and the wide kernel."""
     rng = np.random.default_rng(100 + M)
     for N in (16400, 32800 + 48):
         a, w = random_nvfp4(rng, M, 96), random_nvfp4(rng, N, 96)
