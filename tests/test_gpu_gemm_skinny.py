@@ -53,9 +53,10 @@ def test_skinny_random_codes(M, N, K):
     check_fp32(host(out), y, T, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 5, 20, 40, 64])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 20, 40, 64])
 def test_skinny_wide_weight_tiles(M):
-    """Large N, with one weight tile per wave (M <= 4) and two (M > 4), and the wide kernel."""
+    """Large N: the skinny kernel with one weight tile per wave (M <= 4) and two (M > 4), and the wide
+    kernel."""
     rng = np.random.default_rng(100 + M)
     for N in (16400, 32800 + 48):
         a, w = random_nvfp4(rng, M, 96), random_nvfp4(rng, N, 96)
@@ -64,7 +65,7 @@ def test_skinny_wide_weight_tiles(M):
         check_bf16(out, y, T, f"M={M} N={N}")
 
 
-@pytest.mark.parametrize("M", [9, 40, 64])
+@pytest.mark.parametrize("M", [1, 2, 9, 40, 64])
 @pytest.mark.parametrize("K", [2048 + 16, 8192 + 128, 17408, 17408 + 16 * 7])
 def test_skinny_long_k_splits(M, K):
     """Long K: up to 4 waves per column tile (M <= 32) or up to 8 workgroup K-splits (M > 32), uneven
@@ -95,7 +96,7 @@ def test_wide_decode_workspace_contents_do_not_matter():
         check_fp32(host(out), y, T, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [23, 41])
+@pytest.mark.parametrize("M", [2, 23, 41])
 def test_skinny_padded_strides_and_offsets(M):
     """Inputs that are row slices of wider buffers (strides beyond the row), output with a stride."""
     rng = np.random.default_rng(77 + M)
