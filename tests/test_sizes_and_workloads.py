@@ -55,3 +55,15 @@ def test_bf16_rounding_is_nearest_even():
     f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], dtype=np.float32)
     b = workloads.f32_to_bf16_bits(f)
     assert list(workloads.bf16_bits_to_f32(b)) == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0 + 2 ** -7]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits non-zero before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode != 0
+    assert "one GPU" in res.stderr and res.stdout == ""
