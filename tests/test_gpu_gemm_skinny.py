@@ -183,10 +183,13 @@ def test_path_switch_at_65_rows():
     check_fp32(small, y[:64], T[:64], "M=64")
 
 
+@pytest.mark.parametrize("M", [1, 16, 64])
 @pytest.mark.parametrize("direction", ["up", "down"])
-def test_decode_bf16_activation_pipeline(direction):
-    """Decode step at M = 1 from bf16: GPU global scale and quantizer, then the skinny GEMM, BF16 out."""
-    case = wl.C3(1, direction)
+def test_decode_bf16_activation_pipeline(direction, M):
+    """The decode workloads at full size (up 5120 -> 17408, down 17408 -> 5120) from bf16: GPU global
+    scales and quantizer, then the decode GEMM (skinny kernel at M = 1 and 16, split-K wide kernel at
+    M = 64), BF16 out; every output checked."""
+    case = wl.C3(M, direction)
     x, w = wl.draw_x(case), wl.draw_w(case, 0)
     g_a = np.float32(host(nv.global_scale(dev_bf16(x)))[0])
     g_w = np.float32(host(nv.global_scale(dev_bf16(w)))[0])
@@ -195,5 +198,6 @@ def test_decode_bf16_activation_pipeline(direction):
     (out,) = nv.gemm(ac, as_, float(g_a), wc, ws, [nv.Segment(case.N, float(g_w), out_dtype=torch.bfloat16)])
     rac, ras = oracle.quantize(x, g_a)
     rwc, rws = oracle.quantize(w, g_w)
-    y, T = oracle.gemm_rows(rac, ras, g_a, rwc, rws, [0, case.N], np.array([g_w], np.float32), np.arange(1))
+    assert (host(ac) == rac).all() and (host(as_) == ras).all()
+    y, T = oracle.gemm_rows(rac, ras, g_a, rwc, rws, [0, case.N], np.array([g_w], np.float32), np.arange(M))
     check_bf16(out, y, T, case.name)
