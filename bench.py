@@ -521,8 +521,12 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": gemm_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": gemm_gbps / PEAK_HBM_GBPS}
-    kernel = ("gemm_skinny_kernel" if M <= 32 else "gemm_wide_kernel + gemm_wide_reduce_kernel") if M <= 64 \
-        else "gemm_kernel"
+    if M > 64:
+        kernel = "gemm_kernel"
+    elif M > 32:  # the reduce kernel runs only when K is split over workgroups (the workspace holds the parts)
+        kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if step.workspace is not None else "")
+    else:
+        kernel = "gemm_skinny_kernel"
     tr = measured_traffic(kernel, case.name)
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,

@@ -136,9 +136,9 @@ typedef struct {
  * value times an E4M3 scale is exact in FP16), then scaled once by RN32(g_a * g_w[s]).
  * M == 0 or N == 0 is a no-op; K == 0 writes the epilogue of y = 0.
  * workspace: device scratch of at least nvfp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
- * (may be NULL when that is 0; it is not for 32 < M <= 64, where the split-K partial sums of the
- * decode kernel live there). Owned by the caller; its contents on entry do not matter, and calls
- * that share one workspace must be ordered on one stream.
+ * (may be NULL when that is 0; it is not when 32 < M <= 64 and K is long enough to be split over
+ * workgroups, where the decode kernel's partial sums live there). Owned by the caller; its contents
+ * on entry do not matter, and calls that share one workspace must be ordered on one stream.
  * Errors: NULL, SHAPE, ALIGN, SEGMENTS, SCALE, EPILOGUE, WORKSPACE, HIP.
  */
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
