@@ -129,6 +129,7 @@ typedef struct {
  * nvfp4_gemm -- block-scaled W4A4 GEMM with a per-segment global-scale epilogue.
  *   a_codes/a_scales: device NVFP4 activations [M, K] (strides lda_c, lda_s bytes), global scale g_a;
  *   w_codes/w_scales: device NVFP4 weights [N, K] (strides ldw_c, ldw_s bytes);
+ *   every row stride is below 2^23 bytes (so K < 2^24 for dense codes), else SHAPE;
  *   segs[n_segs]: host array, sorted by n_begin, contiguous, non-overlapping, covering [0, N),
  *                 every n_len > 0, 1 <= n_segs <= NVFP4_MAX_SEGMENTS;
  *   g_w[n_segs]: host array, the weight global scale of each segment (finite, > 0).

@@ -28,6 +28,8 @@ nvfp4_status hip_status(hipError_t e, const char* what) {
     return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr int64_t MAX_GEMM_LD = (int64_t)1 << 23;  // bytes per row of codes or scales, exclusive
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool good_scale(float g) { return std::isfinite(g) && g > 0.0f; }
@@ -121,6 +123,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     if (st != NVFP4_OK) return st;
     st = check_nvfp4(w_codes, ldw_c, w_scales, ldw_s, N, K, "W");
     if (st != NVFP4_OK) return st;
+    // the prefill kernel addresses a 256-row tile of each operand with 32-bit buffer offsets
+    if (lda_c >= MAX_GEMM_LD || lda_s >= MAX_GEMM_LD || ldw_c >= MAX_GEMM_LD || ldw_s >= MAX_GEMM_LD)
+        return fail(NVFP4_ERR_SHAPE, "row strides must be below %lld bytes", (long long)MAX_GEMM_LD);
     if (!segs || !g_w) return fail(NVFP4_ERR_NULL, "segment table or g_w is NULL");
     if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
         return fail(NVFP4_ERR_SEGMENTS, "n_segs = %d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);

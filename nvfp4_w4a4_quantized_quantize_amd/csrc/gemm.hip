@@ -18,18 +18,21 @@
 //    multiply by the block scale; block scales are converted E4M3 -> FP16 two at a time.
 //  * Workgroup tile 256 x 256, K chunk 256, 4 waves as 2 x 2, each wave 128 x 128 = 4 x 4 MFMA tiles
 //    of 32 x 32 accumulated in 256 registers. Codes (4 bits) and scale bytes go from HBM straight
-//    into LDS (global_load_lds, no register staging), double buffered (2 x 72 KB), so each chunk's
-//    loads overlap the previous chunk's 256 MFMAs per wave and LDS holds 4.5 bits per element.
+//    into LDS (buffer loads with the LDS destination, no register staging), double buffered
+//    (2 x 72 KB), so each chunk's loads overlap the previous chunk's 256 MFMAs per wave and LDS holds
+//    4.5 bits per element. The buffer resources cover only a tile's existing rows, so the loads need
+//    no clamping: reads past the end return nothing and address only rows that are never stored.
 //    Code rows are XOR-swizzled in 16-byte pieces so the fragment reads are free of bank conflicts.
-//  * Inside a 64-element sub-chunk, K is permuted identically for A and W (lane half h of the MFMA
-//    takes elements [32h + 8j, 32h + 8j + 8) at step j): each lane reads its 32 codes with one
-//    16-byte LDS read. A sum does not depend on the order of its terms.
+//  * Inside a K chunk, K is permuted identically for A and W: at step j of sub-chunk c, lane half h
+//    of the MFMA takes elements [128h + 32c + 8j, 128h + 32c + 8j + 8), so each lane reads the 32
+//    codes of a sub-chunk with one 16-byte LDS read and its 8 block scales of the chunk with one
+//    8-byte read. A sum does not depend on the order of its terms.
 //  * Tiles are ordered for the 8 XCDs (each with its own L2): workgroup b runs on XCD b % 8, so each
 //    XCD gets a contiguous range of tiles, walked in groups of 8 M-tiles so that concurrently
 //    running tiles share A and W panels in L2.
-//  * Epilogue: accumulators are staged per wave through LDS; whole 32-column groups of a plain
-//    segment are scaled and written with 16-byte stores, other columns (gates, segment boundaries,
-//    the N tail) element by element.
+//  * Epilogue: accumulators are staged per wave through LDS, 64 columns at a time; column ranges of
+//    a plain segment are scaled and written with 16-byte stores, 64 columns (whole 128-byte lines of
+//    bf16) or 32 at a time, other columns (gates, segment boundaries, the N tail) element by element.
 #include "device_common.h"
 
 namespace nvfp4 {
@@ -43,68 +46,74 @@ constexpr int B_CODES = A_CODES + BM * ROW_BYTES;
 constexpr int A_SCALES = B_CODES + BN * ROW_BYTES;
 constexpr int B_SCALES = A_SCALES + BM * 16;
 constexpr int STAGE_BYTES = B_SCALES + BN * 16;  // 73728
-constexpr int EP_PITCH = 36;                     // floats per row of the epilogue staging tile
+constexpr int EP_PITCH = 68;                     // floats per row of the epilogue staging tile
 constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-__device__ __forceinline__ void load_lds16(const uint8_t* g, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (lds_ptr_t)lds, 16, 0, 0);
-}
+// Direct-to-LDS buffer loads. A K chunk is 18 loads per wave ("pieces"): pieces 0-7 are A code row
+// groups, 8-15 W code row groups (lane -> row 8j + lane / 8 of the tile, j = 8 wave + t, 16-byte piece
+// (lane % 8) ^ swz(row)), 16 and 17 the A and W scale rows 64 wave + lane. Each operand's buffer
+// resource covers only the tile's rows that exist, so rows beyond the matrix read outside it and
+// return no data: their products only reach output rows or columns that are never stored. Code
+// pieces of the chunk that crosses K read past the row's K (the next row, or outside the buffer);
+// their block scales are zeroed before use.
+constexpr int BUF_FLAGS = 0x00020000;  // raw buffer resource, 32-bit data format (gfx9 family)
 
-// Direct-to-LDS loads. A K chunk is 18 loads per wave ("pieces"): pieces 0-7 are A code row groups,
-// 8-15 W code row groups (lane -> row 8j + lane / 8 of the tile, j = 8 wave + t, 16-byte piece
-// (lane % 8) ^ swz(row)), 16 and 17 the A and W scale rows 64 wave + lane. Rows beyond the matrix are
-// clamped to its last row: their products only reach output rows or columns that are never stored.
-// In the chunk that crosses K, code pieces starting at or beyond K are read from the row start
-// instead (in bounds); their block scales are zeroed before use.
 struct Loader {
-    const uint8_t* a_codes; const uint8_t* a_scales; const uint8_t* w_codes; const uint8_t* w_scales;
-    int64_t lda_c, lda_s, ldw_c, ldw_s, m0, n0, M, N, K;
-    int wave, lane;
+    __amdgpu_buffer_rsrc_t ra_c, rw_c, ra_s, rw_s;
+    uint32_t lda_c, ldw_c, lda_s, ldw_s;
+    uint32_t va_c, vw_c, va_s, vw_s;  // lane parts of the offsets: row lane / 8 (codes), row lane (scales)
+    uint32_t vq;                      // 16 * ((lane % 8) ^ (lane / 8)): the lane's piece before the XOR with t
+    int wave;
 
-    __device__ __forceinline__ void piece(uint8_t* stage, int pc, int64_t k0) const {
+    __device__ __forceinline__ void piece(uint8_t* stage, int pc, uint32_t k0) const {
         const bool is_a = pc < 8 || pc == 16;
-        const uint8_t* codes = is_a ? a_codes : w_codes;
-        const uint8_t* scales = is_a ? a_scales : w_scales;
-        const int64_t ldc = is_a ? lda_c : ldw_c, lds = is_a ? lda_s : ldw_s;
-        const int64_t row0 = is_a ? m0 : n0, nrows = is_a ? M : N;
-        const bool full_rows = row0 + BM <= nrows;
         if (pc < 16) {
             const int t = pc & 7;
             const int j = wave * 8 + t;  // j & 7 == t, so swz(8j + rsub) == rsub ^ t
-            const int rsub = lane >> 3;
-            const int p = (lane & 7) ^ rsub ^ t;
-            int64_t koff = 16 * p;
-            if (k0 + BK > K && k0 + 32 * p >= K) koff = -(k0 >> 1);
-            const int64_t r = row0 + 8 * j + rsub;
-            const int64_t row = full_rows ? r : (r < nrows ? r : nrows - 1);
-            load_lds16(codes + (k0 >> 1) + row * ldc + koff, stage + (is_a ? A_CODES : B_CODES) + j * 1024);
+            const uint32_t ldc = is_a ? lda_c : ldw_c;
+            const uint32_t voff = (is_a ? va_c : vw_c) + (vq ^ (16u * t));
+            const uint32_t soff = (uint32_t)(8 * j) * ldc + (k0 >> 1);
+            uint8_t* dst = stage + (is_a ? A_CODES : B_CODES) + j * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra_c : rw_c, (lds_ptr_t)dst, 16, (int)voff, (int)soff, 0, 0);
         } else {
-            const int64_t r = row0 + 64 * wave + lane;
-            const int64_t row = full_rows ? r : (r < nrows ? r : nrows - 1);
-            load_lds16(scales + row * lds + (k0 >> 4), stage + (is_a ? A_SCALES : B_SCALES) + wave * 1024);
+            const uint32_t lds = is_a ? lda_s : ldw_s;
+            const uint32_t soff = (uint32_t)(64 * wave) * lds + (k0 >> 4);
+            uint8_t* dst = stage + (is_a ? A_SCALES : B_SCALES) + wave * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra_s : rw_s, (lds_ptr_t)dst, 16, (int)(is_a ? va_s : vw_s),
+                                                     (int)soff, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void all(uint8_t* stage, int64_t k0) const {
+    __device__ __forceinline__ void all(uint8_t* stage, uint32_t k0) const {
 #pragma unroll
         for (int pc = 0; pc < 18; ++pc) piece(stage, pc, k0);
     }
 };
 
-// The two E4M3 scale bytes of (sub-chunk c, lane half lh) as FP16.
-__device__ __forceinline__ half2_t scale_pair(const u32x4& s, int c, int lh) {
-    const uint32_t word = s[c] >> (lh << 4);  // bytes 4c + 2lh, 4c + 2lh + 1
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+// Buffer resource over the existing rows of the tile starting at row0 (at most BM rows of ld bytes;
+// the host keeps ld below 2^23, so BM * ld and every offset fit in 31 bits).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t row0, int64_t nrows,
+                                                            int64_t ld) {
+    const int64_t rows = nrows - row0 < BM ? nrows - row0 : BM;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + row0 * ld), (short)0, (int)(rows * ld),
+                                             BUF_FLAGS);
+}
+
+// The two E4M3 scale bytes of sub-chunk c as FP16: s holds the 8 scale bytes of this lane half's
+// 128 elements of the chunk, and sub-chunk c uses its bytes 2c and 2c + 1.
+__device__ __forceinline__ half2_t scale_pair(const u32x2& s, int c) {
+    return (c & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[c >> 1], 1.0f, true)
+                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[c >> 1], 1.0f, false);
 }
 
 // Codes of sub-chunk c (64 elements) for the 4 A and 4 W fragments of this lane.
 __device__ __forceinline__ void read_codes(u32x4 (&ar)[4], u32x4 (&br)[4], const uint8_t* stage, const int (&a_row)[4],
                                            const int (&b_row)[4], int c, int lh) {
-    const int q = 2 * c + lh;
+    const int q = 4 * lh + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ar[i] = *reinterpret_cast<const u32x4*>(stage + A_CODES + a_row[i] * ROW_BYTES + ((q ^ swz(a_row[i])) << 4));
@@ -112,19 +121,21 @@ __device__ __forceinline__ void read_codes(u32x4 (&ar)[4], u32x4 (&br)[4], const
     }
 }
 
-// Scale rows of a chunk (16 bytes each). When the chunk crosses K, bytes of blocks at or beyond K
-// (nvalid of them are valid) are cleared, so that the code pieces read in their place contribute 0.
-__device__ __forceinline__ void read_scales(u32x4 (&as)[4], u32x4 (&bs)[4], const uint8_t* stage, const int (&a_row)[4],
-                                            const int (&b_row)[4], int nvalid) {
+// This lane half's 8 scale bytes of each fragment row of a chunk (bytes 8 lh .. 8 lh + 7 of the row's
+// 16). When the chunk crosses K, bytes of blocks at or beyond K (nvalid of the row's 16 are valid)
+// are cleared, so that the code pieces read in their place contribute 0.
+__device__ __forceinline__ void read_scales(u32x2 (&as)[4], u32x2 (&bs)[4], const uint8_t* stage, const int (&a_row)[4],
+                                            const int (&b_row)[4], int lh, int nvalid) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        as[i] = *reinterpret_cast<const u32x4*>(stage + A_SCALES + a_row[i] * 16);
-        bs[i] = *reinterpret_cast<const u32x4*>(stage + B_SCALES + b_row[i] * 16);
+        as[i] = *reinterpret_cast<const u32x2*>(stage + A_SCALES + a_row[i] * 16 + 8 * lh);
+        bs[i] = *reinterpret_cast<const u32x2*>(stage + B_SCALES + b_row[i] * 16 + 8 * lh);
     }
-    if (nvalid < 16) {
+    if (nvalid < 16) {  // only the chunk that crosses K; the asm keeps this a branch instead of selects
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int nb = nvalid - 4 * d;  // valid bytes in dword d
+        for (int d = 0; d < 2; ++d) {
+            const int nb = nvalid - 8 * lh - 4 * d;  // valid bytes in this lane's dword d
             const uint32_t mask = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (0xffffffffu >> (32 - 8 * nb)));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -194,24 +205,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
             const int64_t rest = (K - kc * BK) >> 4;
             return rest >= 16 ? 16 : (int)rest;
         };
-        const Loader ld{a_codes, a_scales, w_codes, w_scales, lda_c, lda_s, ldw_c, ldw_s, m0, n0, M, N, K, wave, lane};
+        const uint32_t rsub = lane >> 3;
+        const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, N, ldw_c),
+                        tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, N, ldw_s),
+                        (uint32_t)lda_c, (uint32_t)ldw_c, (uint32_t)lda_s, (uint32_t)ldw_s,
+                        rsub * (uint32_t)lda_c, rsub * (uint32_t)ldw_c, (uint32_t)lane * (uint32_t)lda_s,
+                        (uint32_t)lane * (uint32_t)ldw_s, 16u * ((lane & 7) ^ rsub), wave};
         ld.all(smem, 0);
         // chunk 1 (or chunk 0 again when there is none): pieces 0-7 now, 8-17 during chunk 0's steps 0-4
-        const int64_t k1 = nk > 1 ? BK : 0;
+        const uint32_t k1 = nk > 1 ? BK : 0;
 #pragma unroll
         for (int pc = 0; pc < 8; ++pc) ld.piece(smem + STAGE_BYTES, pc, k1);
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // the 18 loads of chunk 0 landed
         __syncthreads();
 
-        u32x4 ascl[4], bscl[4], araw[4], braw[4], anext[4], bnext[4];
+        u32x2 ascl[4], bscl[4];
+        u32x4 araw[4], braw[4], anext[4], bnext[4];
         half2_t as2[4], bs2[4];
         half8_t aop[2][4], bop[2][4];
-        read_scales(ascl, bscl, smem, a_row, b_row, nvalid_of(0));
+        read_scales(ascl, bscl, smem, a_row, b_row, lh, nvalid_of(0));
         read_codes(araw, braw, smem, a_row, b_row, 0, lh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            as2[i] = scale_pair(ascl[i], 0, lh);
-            bs2[i] = scale_pair(bscl[i], 0, lh);
+            as2[i] = scale_pair(ascl[i], 0);
+            bs2[i] = scale_pair(bscl[i], 0);
             aop[0][i] = dequant8(araw[i][0], as2[i][0]);
             bop[0][i] = dequant8(braw[i][0], bs2[i][0]);
         }
@@ -227,14 +244,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 // at the previous chunk's barrier), chunk kc + 2's pieces 0-7 at steps 12-15 (into the
                 // stage freed at this chunk's barrier); chunk indices clamp to the last chunk
                 if (st <= 4) {
-                    const int64_t k1c = (kc + 1 < nk ? kc + 1 : nk - 1) * BK;
+                    const uint32_t k1c = (uint32_t)((kc + 1 < nk ? kc + 1 : nk - 1) * BK);
                     ld.piece(nxt, 8 + 2 * st, k1c);
                     ld.piece(nxt, 9 + 2 * st, k1c);
                 }
                 if (st == 12) {
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk kc + 1
                     __syncthreads();
-                    read_scales(ascl, bscl, nxt, a_row, b_row, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
+                    read_scales(ascl, bscl, nxt, a_row, b_row, lh, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
                     read_codes(anext, bnext, nxt, a_row, b_row, 0, lh);
                 } else if (j == 0) {
                     read_codes(anext, bnext, cur, a_row, b_row, c + 1, lh);  // sub-chunk c + 1
@@ -246,8 +263,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     for (int i = 0; i < 4; ++i) {
                         araw[i] = anext[i];
                         braw[i] = bnext[i];
-                        as2[i] = scale_pair(ascl[i], c1, lh);
-                        bs2[i] = scale_pair(bscl[i], c1, lh);
+                        as2[i] = scale_pair(ascl[i], c1);
+                        bs2[i] = scale_pair(bscl[i], c1);
                     }
                 }
 #pragma unroll
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     for (int jn = 0; jn < 4; ++jn)
                         acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[cb][i], bop[cb][jn], acc[i][jn], 0, 0, 0);
                 if (st >= 12) {
-                    const int64_t k2c = (kc + 2 < nk ? kc + 2 : nk - 1) * BK;
+                    const uint32_t k2c = (uint32_t)((kc + 2 < nk ? kc + 2 : nk - 1) * BK);
                     ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12), k2c);
                     ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12) + 1, k2c);
                 }
@@ -277,86 +294,117 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     __syncthreads();  // all waves done with the LDS stages before the epilogue reuses them
 
     // ---- epilogue ---------------------------------------------------------------------------------
-    // Each wave stages one 128 x 32 column group of its FP32 accumulators at a time in a private LDS
-    // region (36-float row pitch). A group inside one plain segment is then scaled and written with
-    // 16-byte stores, lane -> row lane / 4 (+16 per pass), columns (lane % 4) * 8 .. + 8; gate segments,
-    // segment boundaries and the N tail go element by element, lane -> column lane % 32.
+    // Each wave stages two of its 128 x 32 column groups (64 columns) of FP32 accumulators at a time
+    // in a private LDS region (68-float row pitch). A 64-column pair inside one plain segment is then
+    // scaled and written with 16-byte stores, lane -> row lane / 8 (+8 per pass), columns
+    // (lane % 8) * 8 .. + 8, so that every row of the pair is written in whole 128-byte lines; other
+    // 32-column groups of a plain segment use the same stores with 4 lanes per row, and gate
+    // segments, segment boundaries and the N tail go element by element, lane -> column lane % 32.
     float* ep = reinterpret_cast<float*>(smem) + wave * (128 * EP_PITCH);
     const int64_t row_base = m0 + wm * 128;
     const int nrows = (int)(M - row_base < 128 ? (M - row_base > 0 ? M - row_base : 0) : 128);
+    auto plain_run = [&](int64_t c0, int width) -> int {  // segment of [c0, c0 + width) if written by vector stores, else -1
+        const int s0 = segment_of(sp, c0);
+        const bool ok = c0 + width <= N && c0 + width - 1 < sp.n_end[s0] && sp.epilogue[s0] == NVFP4_EPI_NONE &&
+                        ((sp.vec_mask >> s0) & 1u) != 0;
+        return ok ? s0 : -1;
+    };
+    auto store8 = [&](uint8_t* outp, bool bf16, int64_t off, f32x4 y0, f32x4 y1) {
+        if (bf16) {
+            u32x4 packed;
+            packed[0] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[0], (__bf16)y0[1]});
+            packed[1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[2], (__bf16)y0[3]});
+            packed[2] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[0], (__bf16)y1[1]});
+            packed[3] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[2], (__bf16)y1[3]});
+            *reinterpret_cast<u32x4*>(outp + off * 2) = packed;
+        } else {
+            *reinterpret_cast<f32x4*>(outp + off * 4) = y0;
+            *reinterpret_cast<f32x4*>(outp + off * 4 + 16) = y1;
+        }
+    };
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
+    for (int jp = 0; jp < 2; ++jp) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ep[(32 * i + (r >> 2) * 8 + lh * 4 + (r & 3)) * EP_PITCH + lr] = acc[i][jn][r];
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ep[(32 * i + (r >> 2) * 8 + lh * 4 + (r & 3)) * EP_PITCH + 32 * h + lr] = acc[i][2 * jp + h][r];
         // the region is private to this wave: its own LDS writes completing is enough
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int64_t c0 = n0 + wn * 128 + 32 * jn;  // first column of this 32-column group
+        const int64_t c0 = n0 + wn * 128 + 64 * jp;  // first column of this 64-column pair
         if (c0 < N) {
-            const int s0 = segment_of(sp, c0);
-            const bool vec = c0 + 32 <= N && c0 + 31 < sp.n_end[s0] && sp.epilogue[s0] == NVFP4_EPI_NONE &&
-                             ((sp.vec_mask >> s0) & 1u) != 0;
-            if (vec) {
-                const float scale = sp.scale[s0];
-                const int64_t ldo = sp.ldo[s0];
-                const bool bf16 = sp.out_dtype[s0] == NVFP4_OUT_BF16;
-                uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s0]);
-                const int64_t j0 = c0 - sp.n_begin[s0] + (lane & 3) * 8;
-                f32x4 v[16];
+            const int s64 = plain_run(c0, 64);
+            if (s64 >= 0) {
+                const float scale = sp.scale[s64];
+                const int64_t ldo = sp.ldo[s64];
+                const bool bf16 = sp.out_dtype[s64] == NVFP4_OUT_BF16;
+                uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s64]);
+                const int64_t j0 = c0 - sp.n_begin[s64] + (lane & 7) * 8;
 #pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const float* src = ep + ((lane >> 2) + 16 * p) * EP_PITCH + (lane & 3) * 8;
-                    v[2 * p] = *reinterpret_cast<const f32x4*>(src);
-                    v[2 * p + 1] = *reinterpret_cast<const f32x4*>(src + 4);
-                }
+                for (int half = 0; half < 2; ++half) {
+                    f32x4 v[16];
 #pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const int rr = (lane >> 2) + 16 * p;
-                    if (rr < nrows) {
-                        const int64_t off = (row_base + rr) * ldo + j0;
-                        const f32x4 y0 = v[2 * p] * scale, y1 = v[2 * p + 1] * scale;
-                        if (bf16) {
-                            u32x4 packed;
-                            packed[0] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[0], (__bf16)y0[1]});
-                            packed[1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[2], (__bf16)y0[3]});
-                            packed[2] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[0], (__bf16)y1[1]});
-                            packed[3] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[2], (__bf16)y1[3]});
-                            *reinterpret_cast<u32x4*>(outp + off * 2) = packed;
-                        } else {
-                            *reinterpret_cast<f32x4*>(outp + off * 4) = y0;
-                            *reinterpret_cast<f32x4*>(outp + off * 4 + 16) = y1;
-                        }
+                    for (int p = 0; p < 8; ++p) {
+                        const float* src = ep + ((lane >> 3) + 8 * (8 * half + p)) * EP_PITCH + (lane & 7) * 8;
+                        v[2 * p] = *reinterpret_cast<const f32x4*>(src);
+                        v[2 * p + 1] = *reinterpret_cast<const f32x4*>(src + 4);
+                    }
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const int rr = (lane >> 3) + 8 * (8 * half + p);
+                        if (rr < nrows) store8(outp, bf16, (row_base + rr) * ldo + j0, v[2 * p] * scale, v[2 * p + 1] * scale);
                     }
                 }
             } else {
-                const int64_t col = c0 + lr;
-                if (col < N) {
-                    const int s = segment_of(sp, col);
-                    const float scale = sp.scale[s];
-                    const int epi = sp.epilogue[s];
-                    const int64_t j = col - sp.n_begin[s];
-                    const int64_t ldo = sp.ldo[s];
-                    const bool f32out = sp.out_dtype[s] == NVFP4_OUT_F32;
-                    uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s]);
-                    float a_coef = 0.0f, dtb = 0.0f;
-                    if (epi == NVFP4_EPI_GDN_DECAY) {
-                        a_coef = expf(sp.A_log[s][j]);
-                        dtb = sp.dt_bias[s][j];
-                    }
-                    for (int rr = lh; rr < nrows; rr += 2) {
-                        const float y = apply_gate(ep[rr * EP_PITCH + lr] * scale, epi, a_coef, dtb);
-                        const int64_t off = (row_base + rr) * ldo + j;
-                        if (f32out)
-                            reinterpret_cast<float*>(outp)[off] = y;
-                        else
-                            reinterpret_cast<__bf16*>(outp)[off] = (__bf16)y;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t c1 = c0 + 32 * h;  // first column of this 32-column group
+                    if (c1 >= N) break;
+                    const int s32 = plain_run(c1, 32);
+                    if (s32 >= 0) {
+                        const float scale = sp.scale[s32];
+                        const int64_t ldo = sp.ldo[s32];
+                        const bool bf16 = sp.out_dtype[s32] == NVFP4_OUT_BF16;
+                        uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s32]);
+                        const int64_t j0 = c1 - sp.n_begin[s32] + (lane & 3) * 8;
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const int rr = (lane >> 2) + 16 * p;
+                            const float* src = ep + rr * EP_PITCH + 32 * h + (lane & 3) * 8;
+                            const f32x4 y0 = *reinterpret_cast<const f32x4*>(src), y1 = *reinterpret_cast<const f32x4*>(src + 4);
+                            if (rr < nrows) store8(outp, bf16, (row_base + rr) * ldo + j0, y0 * scale, y1 * scale);
+                        }
+                    } else {
+                        const int64_t col = c1 + lr;
+                        if (col < N) {
+                            const int s = segment_of(sp, col);
+                            const float scale = sp.scale[s];
+                            const int epi = sp.epilogue[s];
+                            const int64_t j = col - sp.n_begin[s];
+                            const int64_t ldo = sp.ldo[s];
+                            const bool f32out = sp.out_dtype[s] == NVFP4_OUT_F32;
+                            uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s]);
+                            float a_coef = 0.0f, dtb = 0.0f;
+                            if (epi == NVFP4_EPI_GDN_DECAY) {
+                                a_coef = expf(sp.A_log[s][j]);
+                                dtb = sp.dt_bias[s][j];
+                            }
+                            for (int rr = lh; rr < nrows; rr += 2) {
+                                const float y = apply_gate(ep[rr * EP_PITCH + 32 * h + lr] * scale, epi, a_coef, dtb);
+                                const int64_t off = (row_base + rr) * ldo + j;
+                                if (f32out)
+                                    reinterpret_cast<float*>(outp)[off] = y;
+                                else
+                                    reinterpret_cast<__bf16*>(outp)[off] = (__bf16)y;
+                            }
+                        }
                     }
                 }
             }
         }
-        // the next group's staging writes must not pass this group's reads
+        // the next pair's staging writes must not pass this pair's reads
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
