@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     uint16_t* __restrict__ y_out, int64_t ldy) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    if (NBL == 0 && row >= rows) return;
     const int64_t nb = K / 16;
     const uint16_t* xr = x + row * ldx;
     uint8_t* codes_row = codes + row * ldc;
@@ -172,28 +172,23 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     uint16_t* y_row = y_out ? y_out + row * ldy : nullptr;
 
     if constexpr (NBL > 0) {
-        // the row and the matching norm weights are loaded together, so the weights' latency hides
-        // behind the row's and the reduction
-        qu32x4 p[NBL][2], wt[NBL][2];
-        double ss = 0.0;
+        // the row is loaded first; the norm weights are staged once per workgroup in LDS meanwhile
+        __shared__ __attribute__((aligned(16))) uint16_t w_lds[NBL * 64 * 16];
+        qu32x4 p[NBL][2];
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int64_t b = lane + 64 * j;
-            if (b < nb) {
+            if (b < nb && row < rows) {
                 const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
                 p[j][0] = __builtin_nontemporal_load(src);
                 p[j][1] = __builtin_nontemporal_load(src + 1);
             }
         }
-#pragma unroll
-        for (int j = 0; j < NBL; ++j) {
-            const int64_t b = lane + 64 * j;
-            if (b < nb) {
-                const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
-                wt[j][0] = wsrc[0];
-                wt[j][1] = wsrc[1];
-            }
-        }
+        for (int64_t i = threadIdx.x; i < nb * 2; i += 256)
+            reinterpret_cast<qu32x4*>(w_lds)[i] = reinterpret_cast<const qu32x4*>(w)[i];
+        __syncthreads();
+        if (row >= rows) return;
+        double ss = 0.0;
 #pragma unroll
         for (int j = 0; j < NBL; ++j)
             if (lane + 64 * j < nb) ss += sum_squares16(p[j][0], p[j][1]);
@@ -201,7 +196,10 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int64_t b = lane + 64 * j;
-            if (b < nb) norm_encode_block(p[j][0], p[j][1], wt[j][0], wt[j][1], b, r, g, codes_row, scales_row, y_row);
+            if (b < nb) {
+                const qu32x4* wl = reinterpret_cast<const qu32x4*>(w_lds + 16 * b);
+                norm_encode_block(p[j][0], p[j][1], wl[0], wl[1], b, r, g, codes_row, scales_row, y_row);
+            }
         }
     } else {
         double ss = 0.0;
