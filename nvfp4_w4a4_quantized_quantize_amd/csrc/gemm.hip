@@ -27,6 +27,8 @@
 //    of the MFMA takes elements [128h + 32c + 8j, 128h + 32c + 8j + 8), so each lane reads the 32
 //    codes of a sub-chunk with one 16-byte LDS read and its 8 block scales of the chunk with one
 //    8-byte read. A sum does not depend on the order of its terms.
+//  * In a partial last column of tiles, a wave skips the 32-column fragments that lie wholly past N
+//    (no reads, dequantization or matrix instructions for them); its loads and barriers are the same.
 //  * Tiles are ordered for the 8 XCDs (each with its own L2): workgroup b runs on XCD b % 8, so each
 //    XCD gets a contiguous range of tiles, walked in groups of 8 M-tiles so that concurrently
 //    running tiles share A and W panels in L2.
@@ -111,25 +113,30 @@ __device__ __forceinline__ half2_t scale_pair(const u32x2& s, int c) {
 }
 
 // Codes of sub-chunk c (64 elements) for the 4 A and 4 W fragments of this lane.
+// (Only the first NB W fragments, and no A fragment when NB is 0.)
+template <int NB>
 __device__ __forceinline__ void read_codes(u32x4 (&ar)[4], u32x4 (&br)[4], const uint8_t* stage, const int (&a_row)[4],
                                            const int (&b_row)[4], int c, int lh) {
     const int q = 4 * lh + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ar[i] = *reinterpret_cast<const u32x4*>(stage + A_CODES + a_row[i] * ROW_BYTES + ((q ^ swz(a_row[i])) << 4));
-        br[i] = *reinterpret_cast<const u32x4*>(stage + B_CODES + b_row[i] * ROW_BYTES + ((q ^ swz(b_row[i])) << 4));
+        if (NB > 0)
+            ar[i] = *reinterpret_cast<const u32x4*>(stage + A_CODES + a_row[i] * ROW_BYTES + ((q ^ swz(a_row[i])) << 4));
+        if (i < NB)
+            br[i] = *reinterpret_cast<const u32x4*>(stage + B_CODES + b_row[i] * ROW_BYTES + ((q ^ swz(b_row[i])) << 4));
     }
 }
 
 // This lane half's 8 scale bytes of each fragment row of a chunk (bytes 8 lh .. 8 lh + 7 of the row's
 // 16). When the chunk crosses K, bytes of blocks at or beyond K (nvalid of the row's 16 are valid)
-// are cleared, so that the code pieces read in their place contribute 0.
+// are cleared, so that the code pieces read in their place contribute 0. (Fragments as in read_codes.)
+template <int NB>
 __device__ __forceinline__ void read_scales(u32x2 (&as)[4], u32x2 (&bs)[4], const uint8_t* stage, const int (&a_row)[4],
                                             const int (&b_row)[4], int lh, int nvalid) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        as[i] = *reinterpret_cast<const u32x2*>(stage + A_SCALES + a_row[i] * 16 + 8 * lh);
-        bs[i] = *reinterpret_cast<const u32x2*>(stage + B_SCALES + b_row[i] * 16 + 8 * lh);
+        if (NB > 0) as[i] = *reinterpret_cast<const u32x2*>(stage + A_SCALES + a_row[i] * 16 + 8 * lh);
+        if (i < NB) bs[i] = *reinterpret_cast<const u32x2*>(stage + B_SCALES + b_row[i] * 16 + 8 * lh);
     }
     if (nvalid < 16) {  // only the chunk that crosses K; the asm keeps this a branch instead of selects
         asm volatile("" ::: "memory");
@@ -139,11 +146,111 @@ __device__ __forceinline__ void read_scales(u32x2 (&as)[4], u32x2 (&bs)[4], cons
             const uint32_t mask = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (0xffffffffu >> (32 - 8 * nb)));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                as[i][d] &= mask;
-                bs[i][d] &= mask;
+                if (NB > 0) as[i][d] &= mask;
+                if (i < NB) bs[i][d] &= mask;
             }
         }
     }
+}
+
+// The main loop over the nk K chunks (see the kernel) for a wave whose first NJ of its 4 column
+// fragments hold columns below N: 4 in all but a partial last column of tiles, where it is 2 or 0 and
+// the fragments past N are neither read, dequantized nor multiplied. Every wave runs the same loads
+// and barriers.
+template <int NJ>
+__device__ __forceinline__ void main_loop(floatx16 (&acc)[4][4], uint8_t* smem, const Loader& ld, const int (&a_row)[4],
+                                          const int (&b_row)[4], int lh, int64_t nk, int64_t K) {
+    auto nvalid_of = [&](int64_t kc) -> int {
+        const int64_t rest = (K - kc * BK) >> 4;
+        return rest >= 16 ? 16 : (int)rest;
+    };
+    ld.all(smem, 0);
+    // chunk 1 (or chunk 0 again when there is none): pieces 0-7 now, 8-17 during chunk 0's steps 0-4
+    const uint32_t k1 = nk > 1 ? BK : 0;
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) ld.piece(smem + STAGE_BYTES, pc, k1);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // the 18 loads of chunk 0 landed
+    __syncthreads();
+
+    u32x2 ascl[4], bscl[4];
+    u32x4 araw[4], braw[4], anext[4], bnext[4];
+    half2_t as2[4], bs2[4];
+    half8_t aop[2][4], bop[2][4];
+    read_scales<NJ>(ascl, bscl, smem, a_row, b_row, lh, nvalid_of(0));
+    read_codes<NJ>(araw, braw, smem, a_row, b_row, 0, lh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (NJ > 0) {
+            as2[i] = scale_pair(ascl[i], 0);
+            aop[0][i] = dequant8(araw[i][0], as2[i][0]);
+        }
+        if (i < NJ) {
+            bs2[i] = scale_pair(bscl[i], 0);
+            bop[0][i] = dequant8(braw[i][0], bs2[i][0]);
+        }
+    }
+
+    for (int64_t kc = 0; kc < nk; ++kc) {
+        const uint8_t* cur = smem + (kc & 1) * STAGE_BYTES;
+        uint8_t* nxt = smem + ((kc + 1) & 1) * STAGE_BYTES;
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+            const int c = st >> 2, j = st & 3;
+            const int cb = st & 1, nb = cb ^ 1;
+            // loads, two pieces per step: chunk kc + 1's pieces 8-17 at steps 0-4 (into the stage freed
+            // at the previous chunk's barrier), chunk kc + 2's pieces 0-7 at steps 12-15 (into the
+            // stage freed at this chunk's barrier); chunk indices clamp to the last chunk
+            if (st <= 4) {
+                const uint32_t k1c = (uint32_t)((kc + 1 < nk ? kc + 1 : nk - 1) * BK);
+                ld.piece(nxt, 8 + 2 * st, k1c);
+                ld.piece(nxt, 9 + 2 * st, k1c);
+            }
+            if (st == 12) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk kc + 1
+                __syncthreads();
+                read_scales<NJ>(ascl, bscl, nxt, a_row, b_row, lh, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
+                read_codes<NJ>(anext, bnext, nxt, a_row, b_row, 0, lh);
+            } else if (j == 0) {
+                read_codes<NJ>(anext, bnext, cur, a_row, b_row, c + 1, lh);  // sub-chunk c + 1
+            }
+            // operands of the next step (the next chunk's first step after step 15)
+            const int s1 = (st + 1) & 15, c1 = s1 >> 2, j1 = s1 & 3;
+            if (j1 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (NJ > 0) {
+                        araw[i] = anext[i];
+                        as2[i] = scale_pair(ascl[i], c1);
+                    }
+                    if (i < NJ) {
+                        braw[i] = bnext[i];
+                        bs2[i] = scale_pair(bscl[i], c1);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (NJ > 0) aop[nb][i] = dequant8(araw[i][j1], as2[i][j1 >> 1]);
+                if (i < NJ) bop[nb][i] = dequant8(braw[i][j1], bs2[i][j1 >> 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jn = 0; jn < NJ; ++jn)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[cb][i], bop[cb][jn], acc[i][jn], 0, 0, 0);
+            if (st >= 12) {
+                const uint32_t k2c = (uint32_t)((kc + 2 < nk ? kc + 2 : nk - 1) * BK);
+                ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12), k2c);
+                ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12) + 1, k2c);
+            }
+#pragma unroll
+            for (int t = 0; t < 4 * NJ; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, NJ == 4 ? 4 : 6, 0);  // then the VALU
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still target the LDS
 }
 
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
@@ -201,95 +308,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // runs on across the chunk boundary.
     const int64_t nk = (K + BK - 1) / BK;
     if (nk > 0) {
-        auto nvalid_of = [&](int64_t kc) -> int {
-            const int64_t rest = (K - kc * BK) >> 4;
-            return rest >= 16 ? 16 : (int)rest;
-        };
         const uint32_t rsub = lane >> 3;
         const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, N, ldw_c),
                         tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, N, ldw_s),
                         (uint32_t)lda_c, (uint32_t)ldw_c, (uint32_t)lda_s, (uint32_t)ldw_s,
                         rsub * (uint32_t)lda_c, rsub * (uint32_t)ldw_c, (uint32_t)lane * (uint32_t)lda_s,
                         (uint32_t)lane * (uint32_t)ldw_s, 16u * ((lane & 7) ^ rsub), wave};
-        ld.all(smem, 0);
-        // chunk 1 (or chunk 0 again when there is none): pieces 0-7 now, 8-17 during chunk 0's steps 0-4
-        const uint32_t k1 = nk > 1 ? BK : 0;
-#pragma unroll
-        for (int pc = 0; pc < 8; ++pc) ld.piece(smem + STAGE_BYTES, pc, k1);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // the 18 loads of chunk 0 landed
-        __syncthreads();
-
-        u32x2 ascl[4], bscl[4];
-        u32x4 araw[4], braw[4], anext[4], bnext[4];
-        half2_t as2[4], bs2[4];
-        half8_t aop[2][4], bop[2][4];
-        read_scales(ascl, bscl, smem, a_row, b_row, lh, nvalid_of(0));
-        read_codes(araw, braw, smem, a_row, b_row, 0, lh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            as2[i] = scale_pair(ascl[i], 0);
-            bs2[i] = scale_pair(bscl[i], 0);
-            aop[0][i] = dequant8(araw[i][0], as2[i][0]);
-            bop[0][i] = dequant8(braw[i][0], bs2[i][0]);
-        }
-
-        for (int64_t kc = 0; kc < nk; ++kc) {
-            const uint8_t* cur = smem + (kc & 1) * STAGE_BYTES;
-            uint8_t* nxt = smem + ((kc + 1) & 1) * STAGE_BYTES;
-#pragma unroll
-            for (int st = 0; st < 16; ++st) {
-                const int c = st >> 2, j = st & 3;
-                const int cb = st & 1, nb = cb ^ 1;
-                // loads, two pieces per step: chunk kc + 1's pieces 8-17 at steps 0-4 (into the stage freed
-                // at the previous chunk's barrier), chunk kc + 2's pieces 0-7 at steps 12-15 (into the
-                // stage freed at this chunk's barrier); chunk indices clamp to the last chunk
-                if (st <= 4) {
-                    const uint32_t k1c = (uint32_t)((kc + 1 < nk ? kc + 1 : nk - 1) * BK);
-                    ld.piece(nxt, 8 + 2 * st, k1c);
-                    ld.piece(nxt, 9 + 2 * st, k1c);
-                }
-                if (st == 12) {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk kc + 1
-                    __syncthreads();
-                    read_scales(ascl, bscl, nxt, a_row, b_row, lh, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
-                    read_codes(anext, bnext, nxt, a_row, b_row, 0, lh);
-                } else if (j == 0) {
-                    read_codes(anext, bnext, cur, a_row, b_row, c + 1, lh);  // sub-chunk c + 1
-                }
-                // operands of the next step (the next chunk's first step after step 15)
-                const int s1 = (st + 1) & 15, c1 = s1 >> 2, j1 = s1 & 3;
-                if (j1 == 0) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        araw[i] = anext[i];
-                        braw[i] = bnext[i];
-                        as2[i] = scale_pair(ascl[i], c1);
-                        bs2[i] = scale_pair(bscl[i], c1);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    aop[nb][i] = dequant8(araw[i][j1], as2[i][j1 >> 1]);
-                    bop[nb][i] = dequant8(braw[i][j1], bs2[i][j1 >> 1]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int jn = 0; jn < 4; ++jn)
-                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[cb][i], bop[cb][jn], acc[i][jn], 0, 0, 0);
-                if (st >= 12) {
-                    const uint32_t k2c = (uint32_t)((kc + 2 < nk ? kc + 2 : nk - 1) * BK);
-                    ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12), k2c);
-                    ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12) + 1, k2c);
-                }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then four VALU
-                }
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still target the LDS
+        const int64_t wcol0 = n0 + wn * 128;  // first column of this wave's fragments
+        if (wcol0 + 64 < N)
+            main_loop<4>(acc, smem, ld, a_row, b_row, lh, nk, K);
+        else if (wcol0 < N)
+            main_loop<2>(acc, smem, ld, a_row, b_row, lh, nk, K);
+        else
+            main_loop<0>(acc, smem, ld, a_row, b_row, lh, nk, K);
     }
     __syncthreads();  // all waves done with the LDS stages before the epilogue reuses them
 
