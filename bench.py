@@ -250,6 +250,18 @@ def _time_loop(fn, n: int) -> float:
     return a.elapsed_time(b) / n
 
 
+def _settle(fn, seconds: float = 0.2) -> None:
+    """Untimed: call fn(i) back to back for about `seconds` of wall time, so that the GPU's clocks have
+    left their idle state before a kernel of a fraction of a millisecond is timed."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def copy_ceiling_gbps(mb: int = 1024, reps: int = 10) -> float:
     """Bytes moved (read + write) per second by a plain device-to-device copy of `mb` MiB: the
     practical streaming ceiling of HBM on this machine, reported beside the nominal peak."""
@@ -351,7 +363,9 @@ def bench_rmsnorm_quantize(steps: int, warmup: int, cpu: bool) -> dict:
         fused(i)
         unfused(i)
     torch.cuda.synchronize()
+    _settle(fused)
     f_ms = _time_loop(fused, steps)
+    _settle(unfused)
     u_ms = _time_loop(unfused, steps)
     alg = rows * K * (2.0 + 0.5625) + 2 * K
     f_gbps = alg / (f_ms * 1e-3) / 1e9
