@@ -373,6 +373,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 const bool bf16 = sp.out_dtype[s64] == NVFP4_OUT_BF16;
                 uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s64]);
                 const int64_t j0 = c0 - sp.n_begin[s64] + (lane & 7) * 8;
+                if (nrows == 128 && bf16) {  // full rows, bf16: no per-row masks, no per-store type test
+                    uint8_t* dst = outp + ((row_base + (lane >> 3)) * ldo + j0) * 2;
+                    const int64_t step8 = 8 * ldo * 2;  // bytes between a lane's consecutive rows
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        f32x4 v[16];
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const float* src = ep + ((lane >> 3) + 8 * (8 * half + p)) * EP_PITCH + (lane & 7) * 8;
+                            v[2 * p] = *reinterpret_cast<const f32x4*>(src);
+                            v[2 * p + 1] = *reinterpret_cast<const f32x4*>(src + 4);
+                        }
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const f32x4 y0 = v[2 * p] * scale, y1 = v[2 * p + 1] * scale;
+                            u32x4 packed;
+                            packed[0] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[0], (__bf16)y0[1]});
+                            packed[1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[2], (__bf16)y0[3]});
+                            packed[2] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[0], (__bf16)y1[1]});
+                            packed[3] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[2], (__bf16)y1[3]});
+                            *reinterpret_cast<u32x4*>(dst + (8 * half + p) * step8) = packed;
+                        }
+                    }
+                } else
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     f32x4 v[16];
