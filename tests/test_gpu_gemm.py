@@ -145,6 +145,30 @@ def test_output_guard_bands_and_strides():
     check_fp32(b[1:M + 1, 4:4 + N], y, T, "strided output")
 
 
+def test_row_strides_just_below_the_limit():
+    """Codes and scale rows of both operands strided by 2^23 - 16 bytes, the largest stride accepted:
+    the prefill kernel's 32-bit buffer offsets (up to 255 strides inside a tile) and record counts
+    stay in range. The padding holds 0xFF bytes (NaN as an E4M3 scale), read in the chunk that
+    crosses K and masked there."""
+    rng = np.random.default_rng(23)
+    M, N, K = 300, 70, 272  # a ragged second M tile, a ragged N tile, a K tail of one block
+    a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
+    ld = (1 << 23) - 16
+
+    def strided(x):
+        rows, cols = x.shape
+        buf = torch.full((rows, ld), 0xFF, dtype=torch.uint8, device=DEV)
+        buf[:, :cols] = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+        return buf[:, :cols]
+    ac, as_, wc, ws = strided(a[0]), strided(a[1]), strided(w[0]), strided(w[1])
+    assert ac.stride(0) == ld and ws.stride(0) == ld
+    (out,) = nv.gemm(ac, as_, 0.25, wc, ws, [nv.Segment(N, 3.0)])
+    (y, T), _ = oracle_y(a, w, 0.25, [(N, 3.0, "none", torch.float32, None, None)], np.arange(M))
+    check_fp32(host(out), y, T, "strides 2^23 - 16")
+    del ac, as_, wc, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("M", [5, 40, 70])
 def test_k_zero_writes_zero_and_empty_shapes(M):
     """K = 0 on each kernel (skinny, split-K decode, tiled): the epilogue of y = 0."""
