@@ -262,6 +262,35 @@ def _settle(fn, seconds: float = 0.2) -> None:
     torch.cuda.synchronize()
 
 
+def library_gemm(step: Step, M: int, N: int, K: int, rounds: int = 4, reps: int = 10) -> dict:
+    """Dense FP16 and BF16 GEMMs of the same shape through torch.matmul (hipBLASLt on ROCm), timed in
+    rounds alternating with the NVFP4 GEMM of `step`: a same-process, same-clock comparison. The dense
+    operands are random normal; the library GEMMs dequantize nothing and have no segment epilogue."""
+    a16 = torch.randn(M, K, device="cuda", dtype=torch.float16)
+    w16 = torch.randn(N, K, device="cuda", dtype=torch.float16)
+    y16 = torch.empty(M, N, device="cuda", dtype=torch.float16)
+    abf, wbf = a16.to(torch.bfloat16), w16.to(torch.bfloat16)
+    ybf = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    runs = {"nvfp4_gemm": lambda i: step.gemm(),
+            "fp16_matmul": lambda i: torch.matmul(a16, w16.t(), out=y16),
+            "bf16_matmul": lambda i: torch.matmul(abf, wbf.t(), out=ybf)}
+    times = {k: [] for k in runs}
+    for _ in range(rounds):
+        for k, fn in runs.items():
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            times[k].append(_time_loop(fn, reps))
+    flops = 2.0 * M * N * K
+    res = {k: {"best_ms": min(v), "tflops": flops / (min(v) * 1e-3) / 1e12} for k, v in times.items()}
+    log("[gpu] same process: " + ", ".join(f"{k} {v['best_ms']:.3f} ms ({v['tflops']:.0f} TFLOP/s)"
+                                           for k, v in res.items()))
+    del a16, w16, y16, abf, wbf, ybf
+    torch.cuda.empty_cache()
+    res["note"] = "best of 4 rounds of 10 back-to-back calls; torch.matmul on dense random operands"
+    return res
+
+
 def copy_ceiling_gbps(mb: int = 1024, reps: int = 10) -> float:
     """Bytes moved (read + write) per second by a plain device-to-device copy of `mb` MiB: the
     practical streaming ceiling of HBM on this machine, reported beside the nominal peak."""
@@ -481,6 +510,9 @@ def main() -> int:
                     help="overwrite a buffer of this size before each step (-1: none)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on dense FP16 and BF16 operands of the same "
+                         "shape, alternating with the NVFP4 GEMM in this process")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the hot path has no multi-GPU part here (asked for --gpus {args.gpus}).",
@@ -572,6 +604,8 @@ def main() -> int:
                               "algorithmic_bytes": q_bytes, "copy_ceiling_gbps": copy_gbps,
                               "frac_of_copy_ceiling": q_gbps / copy_gbps},
     }
+    if args.library_gemm:
+        out["library_gemm"] = library_gemm(step, M, N, K)
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on a sample")
         out["cpu_baseline"] = run_cpu_baseline(step, min(args.cpu_rows_quant, M), min(args.cpu_rows_gemm, M))
