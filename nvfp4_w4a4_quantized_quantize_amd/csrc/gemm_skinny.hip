@@ -249,30 +249,34 @@ int skinny_waves(int64_t K) {
 // ---------------------------------------------------------------------------------------------------
 // 32 < M <= 64 ("wide" decode). With three or four activation tiles every weight tile of the kernel
 // above re-reads all activation rows of its K range and dequantizes them, which is then what bounds
-// it. Here a workgroup of 8 waves takes 128 weight rows (two 16-row tiles per wave) and one range of
-// K: its two "K-groups" of 4 waves take alternate 256-element chunks of that range, so each SIMD holds
-// two waves (one's dequantization overlaps the other's matrix instructions) and twice the loads are
-// in flight. Within a K-group each activation chunk is dequantized once, by the group's 256 threads,
-// into LDS as FP16 in the matrix instruction's operand order (wave u converts activation tile u, each
-// lane the 64 elements it would hold itself), and all four waves read their B operands from there;
-// a wave dequantizes only its own weight rows. Loads run two chunks ahead. The K-groups' sums are
+// it. Here a workgroup takes one range of K and 128, 80 or 64 weight rows: two "K-groups" of WPG
+// waves (4, 5 or 4) with NT 16-row weight tiles each (2, 1 or 1); the shape is chosen from N and the
+// split count so that the workgroups fill the CUs (wide_shape). The K-groups take alternate
+// 256-element chunks of the range, so each SIMD holds two or three waves (one's dequantization
+// overlaps another's matrix instructions) and twice the loads are in flight. Within a K-group each
+// activation chunk is dequantized once into LDS as FP16 in the matrix instruction's operand order
+// (wave u converts activation tile u, each lane the 64 elements it would hold itself; a fifth wave
+// converts a clamped copy into a tile that is never read), and all waves read their B operands from
+// there; a wave dequantizes only its own weight rows. Loads run two chunks ahead. The K-groups' sums are
 // added in LDS (group 0 + group 1). K is split across workgroups by a count chosen from K alone: with
 // one split the workgroup applies the segment epilogue itself, else it writes its partial sums (FP32,
 // [split][n][64 activation rows]) to the workspace and a second kernel adds the splits in order and
 // applies the epilogue. Every output bit is thus the same for any N, column group or segment table.
 
-constexpr int WIDE_NT = 2;                   // weight tiles of 16 rows per wave
-constexpr int WIDE_ROWS = 4 * 16 * WIDE_NT;  // weight rows per workgroup
 constexpr int WIDE_MP = 64;                  // activation rows held (M <= 64)
 constexpr int WIDE_SLOTS = 3;                // register ring: K-group chunk i in slot i % 3, loads 2 chunks ahead
 constexpr int WIDE_KG = 2;                   // K-groups of 4 waves per workgroup
 
 // One K-group's FP16 activation chunk: [tile u][step j][lane] -> the 8 values lane (g, r) feeds at
-// step j for activation row 16u + r (elements 64g + 8j .. + 7 of the chunk).
-typedef half8_t ActChunk[4][8][64];
+// step j for activation row 16u + r (elements 64g + 8j .. + 7 of the chunk). A K-group of WPG waves
+// has WPG tiles: tiles 0-3 hold the (at most 64) activation rows; a fifth wave's tile is written and
+// never read.
+template <int WPG>
+using ActChunk = half8_t[WPG][8][64];
 
 // Lane (g, r) of wave u converts its fragment of activation row 16u + r into the chunk.
-__device__ __forceinline__ void stage_act(ActChunk& dst, const RowFrag& f, int u, int lane) {
+template <int WPG>
+__device__ __forceinline__ void stage_act(ActChunk<WPG>& dst, const RowFrag& f, int u, int lane) {
     half2_t sa[2];
     sa[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
     sa[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
@@ -280,10 +284,11 @@ __device__ __forceinline__ void stage_act(ActChunk& dst, const RowFrag& f, int u
     for (int j = 0; j < 8; ++j) dst[u][j][lane] = dequant8(f.c[j >> 2][j & 3], sa[j >> 2][(j >> 1) & 1]);
 }
 
-// The MT x WIDE_NT tiles of one chunk: weights dequantized here, activations read from the chunk.
-template <int MT>
-__device__ __forceinline__ void compute_lds(const RowFrag (&w)[WIDE_NT], const ActChunk& act, int lane,
-                                            f32x4 (&acc)[WIDE_NT][MT]) {
+// The MT x NT tiles of one chunk: weights dequantized here, activations read from the chunk.
+template <int MT, int NT, int WPG>
+__device__ __forceinline__ void compute_lds(const RowFrag (&w)[NT], const ActChunk<WPG>& act, int lane,
+                                            f32x4 (&acc)[NT][MT]) {
+    constexpr int WIDE_NT = NT;
     half2_t sw[WIDE_NT][2];
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) {
@@ -310,12 +315,13 @@ __device__ __forceinline__ void compute_lds(const RowFrag (&w)[WIDE_NT], const A
 // convert the activations of chunk i + 1 into the other buffer. A chunk index at or past c_fhi (a
 // repeat of the last full chunk) gets zero weight scales, which adds exact zeros. There is no branch
 // in here: a load under one is issued where its value is used, or waited for at the join.
-template <int MT, bool LOADS>
+template <int MT, int NT, int WPG, bool LOADS>
 __device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c_fhi, int64_t cl,
-                                          RowFrag (&wf)[WIDE_SLOTS][WIDE_NT], RowFrag (&af)[WIDE_SLOTS],
-                                          ActChunk* act, f32x4 (&acc)[WIDE_NT][MT], const uint8_t* ac,
-                                          const uint8_t* as, const uint8_t* const (&wc)[WIDE_NT],
-                                          const uint8_t* const (&ws)[WIDE_NT], int u, int lane) {
+                                          RowFrag (&wf)[WIDE_SLOTS][NT], RowFrag (&af)[WIDE_SLOTS],
+                                          ActChunk<WPG>* act, f32x4 (&acc)[NT][MT], const uint8_t* ac,
+                                          const uint8_t* as, const uint8_t* const (&wc)[NT],
+                                          const uint8_t* const (&ws)[NT], int u, int lane) {
+    constexpr int WIDE_NT = NT;
     const int dn = (d + 2) % WIDE_SLOTS;
     if constexpr (LOADS) {
         load_full(ac, as, cl, af[dn]);
@@ -327,27 +333,32 @@ __device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c
     const bool live = c < c_fhi;
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) wf[d][t].s = live ? wf[d][t].s : 0u;
-    compute_lds<MT>(wf[d], act[i & 1], lane, acc);
-    stage_act(act[(i + 1) & 1], af[(d + 1) % WIDE_SLOTS], u, lane);
+    compute_lds<MT, NT, WPG>(wf[d], act[i & 1], lane, acc);
+    stage_act<WPG>(act[(i + 1) & 1], af[(d + 1) % WIDE_SLOTS], u, lane);
     // keep the next chunk's dequantization out of this one (it would wait for its loads)
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MT>
-__global__ __launch_bounds__(512) void gemm_wide_kernel(
+// A workgroup is two K-groups of WPG waves, each wave NT weight tiles of 16 rows: WPG * 16 * NT
+// weight rows.
+template <int MT, int NT, int WPG>
+__global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
     const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
     const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
     int64_t M, int64_t N, int64_t K, int64_t per, float* __restrict__ partial, const SegParams sp) {
-    // two FP16 activation buffers per K-group (128 KB); reused at the end for the cross-group sum and
-    // the output tile
-    __shared__ ActChunk lds[WIDE_KG][2];
+    constexpr int WIDE_NT = NT;
+    constexpr int WIDE_ROWS = WPG * 16 * NT;  // weight rows per workgroup
+    constexpr int THREADS = 128 * WPG;
+    // two FP16 activation buffers per K-group (32 WPG KB); reused at the end for the cross-group sum
+    // and the output tile
+    __shared__ ActChunk<WPG> lds[WIDE_KG][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int kg = wave >> 2, u = wave & 3;
+    const int kg = wave / WPG, u = wave % WPG;
     const int r = lane & 15, g = lane >> 4;
     const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
     const int64_t grp = blockIdx.x % groups;
     const int split = (int)(blockIdx.x / groups);
-    const int64_t n0 = grp * WIDE_ROWS + u * (16 * WIDE_NT);
+    const int64_t n0 = grp * WIDE_ROWS + u * (16 * NT);
 
     // weight rows past N and activation rows past M are clamped to the last row: their results are
     // never stored
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(
 #pragma unroll
         for (int uu = 0; uu < MT; ++uu) acc[t][uu] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    ActChunk* act = lds[kg];
+    ActChunk<WPG>* act = lds[kg];
     if (steps > 0) {
         RowFrag wf[WIDE_SLOTS][WIDE_NT], af[WIDE_SLOTS];
         // step by step, in the loop's order, so that the loop's waits count the same loads on entry
@@ -387,19 +398,20 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(
         load_full(ac, as, clamped(1), af[1]);
 #pragma unroll
         for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], clamped(1), wf[1][t]);
-        stage_act(act[0], af[0], u, lane);
+        stage_act<WPG>(act[0], af[0], u, lane);
         int64_t i0 = 0;
         for (; i0 + WIDE_SLOTS <= steps; i0 += WIDE_SLOTS) {
 #pragma unroll
             for (int d = 0; d < WIDE_SLOTS; ++d)
-                wide_step<MT, true>(d, i0 + d, chunk(i0 + d), c_fhi, clamped(i0 + d + 2), wf, af, act, acc, ac, as,
-                                    wc, ws, u, lane);
+                wide_step<MT, NT, WPG, true>(d, i0 + d, chunk(i0 + d), c_fhi, clamped(i0 + d + 2), wf, af, act,
+                                             acc, ac, as, wc, ws, u, lane);
         }
         // the last one or two steps: their chunks are already loaded (slots 0 and 1)
         if (i0 < steps)
-            wide_step<MT, false>(0, i0, chunk(i0), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
+            wide_step<MT, NT, WPG, false>(0, i0, chunk(i0), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
         if (i0 + 1 < steps)
-            wide_step<MT, false>(1, i0 + 1, chunk(i0 + 1), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
+            wide_step<MT, NT, WPG, false>(1, i0 + 1, chunk(i0 + 1), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u,
+                                          lane);
     }
     if (c_fhi < c_hi) {
         // the chunk that crosses K (only in the last split), multiplied by K-group 0
@@ -410,10 +422,10 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(
             load_tail(ac, as, c_fhi, g, K, taf);
 #pragma unroll
             for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, g, K, twf[t]);
-            stage_act(act[0], taf, u, lane);
+            stage_act<WPG>(act[0], taf, u, lane);
         }
         __syncthreads();
-        if (kg == 0) compute_lds<MT>(twf, act[0], lane, acc);
+        if (kg == 0) compute_lds<MT, NT, WPG>(twf, act[0], lane, acc);
     }
 
     // K-group 0 + K-group 1, through LDS. acc[t][uu] of lane (g, r) holds y[n0 + 16t + 4g + e][16uu + r].
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(
 #pragma unroll
                 for (int uu = 0; uu < MT; ++uu)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) tile[16 * uu + r][u * 32 + 16 * t + 4 * g + e] = acc[t][uu][e];
+                    for (int e = 0; e < 4; ++e) tile[16 * uu + r][u * 16 * NT + 16 * t + 4 * g + e] = acc[t][uu][e];
         }
         __syncthreads();
         // a thread keeps one column and walks every fourth row
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(
         const int64_t n = grp * WIDE_ROWS + nl;
         if (n < N) {
             const ColumnOut co = column_out(sp, n);
-            for (int m = tid / WIDE_ROWS; m < rows; m += 512 / WIDE_ROWS) column_store(co, m, tile[m][nl]);
+            for (int m = tid / WIDE_ROWS; m < rows; m += THREADS / WIDE_ROWS) column_store(co, m, tile[m][nl]);
         }
     } else if (kg == 0) {
         // partial[split][n][m]
@@ -532,6 +544,43 @@ static WideSplit wide_split(int64_t K) {
     return {per, (int)((nch + per - 1) / per)};
 }
 
+// Weight rows per workgroup of the wide kernel: 128 (4 waves of 2 tiles per K-group), 80 (5 waves of
+// 1 tile) or 64 (4 waves of 1 tile), whichever gives the fewest rounds of workgroups over the CUs
+// times the busiest SIMD's tiles per chunk (4, 3, 2). Only the grouping of columns changes: every
+// column's sum runs in the same order in all three, so the output bits do not depend on the choice.
+struct WideShape {
+    int rows, wpg, nt;
+};
+
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+static WideShape wide_shape(int64_t N, int splits) {
+    static constexpr WideShape shapes[3] = {{128, 4, 2}, {80, 5, 1}, {64, 4, 1}};
+    static constexpr int load[3] = {4, 3, 2};
+    const int64_t cus = device_cus();
+    int best = 0;
+    int64_t best_cost = -1;
+    for (int s = 0; s < 3; ++s) {
+        const int64_t wgs = (N + shapes[s].rows - 1) / shapes[s].rows * splits;
+        const int64_t cost = (wgs + cus - 1) / cus * load[s];
+        if (best_cost < 0 || cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return shapes[best];
+}
+
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || N <= 0 || K < 0) return 0;
     const int splits = wide_split(K).splits;
@@ -545,13 +594,22 @@ hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t
     if (M == 0 || N == 0) return hipSuccess;
     const WideSplit ks = wide_split(K);
     if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || (ks.splits > 1 && !workspace)) return hipErrorInvalidValue;
-    const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
+    const WideShape sh = wide_shape(N, ks.splits);
+    const int64_t groups = (N + sh.rows - 1) / sh.rows;
     if (groups * ks.splits > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     float* partial = static_cast<float*>(workspace);
     const int mt = (int)((M + 15) / 16);
-    hipLaunchKernelGGL(mt == 3 ? gemm_wide_kernel<3> : gemm_wide_kernel<4>, dim3((uint32_t)(groups * ks.splits)),
-                       dim3(512), 0, stream, a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N,
-                       K, ks.per, partial, sp);
+    using wide_fn = void (*)(const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*, int64_t,
+                             const uint8_t*, int64_t, int64_t, int64_t, int64_t, int64_t, float*, const SegParams);
+    wide_fn fn;
+    if (sh.wpg == 4 && sh.nt == 2)
+        fn = mt == 3 ? gemm_wide_kernel<3, 2, 4> : gemm_wide_kernel<4, 2, 4>;
+    else if (sh.wpg == 5)
+        fn = mt == 3 ? gemm_wide_kernel<3, 1, 5> : gemm_wide_kernel<4, 1, 5>;
+    else
+        fn = mt == 3 ? gemm_wide_kernel<3, 1, 4> : gemm_wide_kernel<4, 1, 4>;
+    hipLaunchKernelGGL(fn, dim3((uint32_t)(groups * ks.splits)), dim3(128 * sh.wpg), 0, stream, a_codes, lda_c,
+                       a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, ks.per, partial, sp);
     if (ks.splits > 1) {
         using reduce_fn = void (*)(const float*, int64_t, int64_t, const SegParams&, hipStream_t);
         static constexpr reduce_fn reduce[8] = {launch_reduce<1>, launch_reduce<2>, launch_reduce<3>,
