@@ -78,6 +78,26 @@ def test_skinny_long_k_splits(M, K):
     check_fp32(host(out), y, T, f"M={M} K={K}")
 
 
+@pytest.mark.parametrize("direction", ["up", "down"])
+def test_wide_workgroup_shapes_agree_bitwise(direction):
+    """For 32 < M <= 64 the rows per workgroup follow N and the K split count (128, 80 or 64): on a
+    256-CU MI355X the MLP up projection (N = 17408, one split) takes 80-row workgroups, the down
+    projection (N = 5120, six splits) 128-row ones, and their first 300 weight rows as a GEMM of
+    their own 64-row ones. Every column's sum runs in the same order in all shapes, so the shared
+    columns agree bit for bit; the full result also meets the oracle's bound on sampled rows."""
+    M = 64
+    N, K = (17408, 5120) if direction == "up" else (5120, 17408)
+    rng = np.random.default_rng(N + K)
+    a = random_nvfp4(rng, M, K, 0x30, 0x70)
+    w = random_nvfp4(rng, N, K, 0x30, 0x70)
+    full = run_single(a, w, 0.02, 0.5)
+    part = run_single(a, (w[0][:300], w[1][:300]), 0.02, 0.5)
+    assert torch.equal(full[:, :300].contiguous().view(torch.int32), part.contiguous().view(torch.int32))
+    rows = np.array([0, 31, 63])
+    y, T = oracle.gemm_rows(a[0], a[1], np.float32(0.02), w[0], w[1], [0, N], np.array([0.5], np.float32), rows)
+    check_fp32(host(full)[rows], y, T, f"{direction} M=64 sampled rows")
+
+
 def test_wide_decode_workspace_contents_do_not_matter():
     """M in (32, 64] with K long enough for two K splits: the partial sums go to the caller's workspace.
     One workspace, filled with NaN first, serves two calls in a row (the second with fewer rows,
