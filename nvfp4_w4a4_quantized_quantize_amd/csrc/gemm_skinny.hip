@@ -27,6 +27,7 @@
 //  * The KW partial sums meet in LDS and are added in wave order (deterministic), then scaled by
 //    g_a * g_w of the column's segment, gated and stored, consecutive threads on consecutive columns.
 #include <algorithm>
+#include <atomic>
 
 #include "device_common.h"
 
@@ -552,16 +553,17 @@ struct WideShape {
     int rows, wpg, nt;
 };
 
+// CUs of the current device, read once per device (concurrent first calls store the same value).
 static int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 static WideShape wide_shape(int64_t N, int splits) {
