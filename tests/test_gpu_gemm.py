@@ -169,6 +169,38 @@ def test_row_strides_just_below_the_limit():
     torch.cuda.empty_cache()
 
 
+def sweep_shapes():
+    """Seeded shapes across the three GEMM kernels: M in the skinny (<= 32), wide (33..64) and tiled
+    (> 64) ranges, N ragged against every column grouping (16, 32, 64, 80, 128, 256), K with tails
+    and, for the wide kernel, long enough to be split over workgroups."""
+    rng = np.random.default_rng(2026)
+    shapes = []
+    for i in range(36):
+        M = int(rng.choice([1, 3, 17, 32, 33, 47, 64, 65, 130, 257]))
+        N = int(rng.integers(1, 400)) if i % 3 else int(rng.integers(400, 2600))
+        K = 16 * int(rng.integers(1, 160)) if i % 4 else 16 * int(rng.integers(300, 420))
+        shapes.append((M, N, K))
+    return shapes
+
+
+@pytest.mark.parametrize("M,N,K", sweep_shapes())
+def test_random_shape_sweep(M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    a, w = random_nvfp4(rng, M, K, 0x20, 0x58), random_nvfp4(rng, N, K, 0x20, 0x58)
+    n1 = max(1, N // 3)
+    spec = [(n1, 0.75, "none", torch.bfloat16, None, None)]
+    if N - n1 > 0:
+        spec.append((N - n1, 1.5, "none", torch.float32, None, None))
+    outs = run_gemm(a, w, np.float32(0.03), spec, K)
+    (y, T), bounds = oracle_y(a, w, np.float32(0.03), spec, np.arange(M))
+    for s, out in enumerate(outs):
+        lo, hi = bounds[s], bounds[s + 1]
+        if spec[s][3] == torch.float32:
+            check_fp32(host(out), y[:, lo:hi], T[:, lo:hi], f"M={M} N={N} K={K} segment {s}")
+        else:
+            check_bf16(out, y[:, lo:hi], T[:, lo:hi], f"M={M} N={N} K={K} segment {s}")
+
+
 @pytest.mark.parametrize("M", [5, 40, 70])
 def test_k_zero_writes_zero_and_empty_shapes(M):
     """K = 0 on each kernel (skinny, split-K decode, tiled): the epilogue of y = 0."""
