@@ -10,8 +10,11 @@ before timing. Inputs are resident in HBM when the timed region starts.
 
 Prints one JSON line. `value` is the step's throughput in GEMM TFLOP/s (2 M N K per step time);
 `roofline` describes the dominant kernel (the GEMM) against the dense FP16 MFMA peak it runs on;
-`roofline_quantize` the quantizer against HBM bandwidth; `cpu_baseline` the CPU oracle on a bounded
-sample of the same step, extrapolated linearly in M.
+`roofline_quantize` the quantizer against HBM bandwidth, timed over three rotating copies of the
+activation (1 GB of input per round, more than the last-level cache); `cpu_baseline` the CPU oracle on
+a bounded sample of the same step, extrapolated linearly in M, on all host threads and on one;
+`other_configs` the GEMMs of the other workloads (prefill projection, fused MLP gate+up, the six
+decode GEMMs), each over rotating weight copies, with its own roofline.
 """
 from __future__ import annotations
 
@@ -176,6 +179,95 @@ def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
             "gemm_ms_med": float(np.median(g_ms))}
 
 
+def time_quantizer_rotating(step: Step, copies: int = 3, reps: int = 10) -> dict:
+    """The quantizer over `copies` distinct activation tensors (and as many output buffers) in turn,
+    back to back: with three copies of the 32K-token activation that is 1.0 GB of input per round,
+    four times the 256 MB last-level cache, so every launch streams its input from HBM."""
+    xs = [step.x] + [step.x.clone() for _ in range(copies - 1)]
+    outs = [(step.a_codes, step.a_scales)] + [nv.alloc_nvfp4(step.case.M, step.case.K, "cuda")
+                                              for _ in range(copies - 1)]
+    fn = lambda i: nv.quantize(xs[i % copies], step.g_a, *outs[i % copies])  # noqa: E731
+    for i in range(2 * copies):
+        fn(i)
+    torch.cuda.synchronize()
+    ms = _time_loop(fn, reps * copies)
+    in_bytes = copies * step.case.M * step.case.K * 2
+    del xs, outs
+    torch.cuda.empty_cache()
+    return {"ms": ms, "rotation_bytes": in_bytes, "copies": copies, "launches": reps * copies}
+
+
+def gemm_roofline(case: wl.GemmCase, ms: float) -> dict:
+    """TFLOP/s, GB/s and the roofline the GEMM of `case` runs against: the dense FP16 MFMA peak above
+    the ridge point (peak FLOP/s per HBM byte/s), HBM bandwidth below it."""
+    M, N, K = case.M, case.N, case.K
+    flops = 2.0 * M * N * K
+    out_bytes = sum(M * s.n * (4 if s.out_dtype == wl.OUT_F32 else 2) for s in case.segments)
+    nbytes = 0.5625 * (M + N) * K + out_bytes  # codes + scales of A and W, plus the outputs
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    if flops / nbytes >= PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_F16_MFMA_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS}
+    if M > 64:
+        kernel = "gemm_kernel"
+    elif M > 32:
+        kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if nv.lib().nvfp4_gemm_workspace_bytes(M, N, K)
+                                       else "")
+    else:
+        kernel = "gemm_skinny_kernel"
+    roof.update({"kernel": kernel, "avg_ms": ms, "algorithmic_flop": flops, "algorithmic_bytes": nbytes})
+    return {"ms": ms, "tflops": tflops, "gbps": gbps, "roofline": roof}
+
+
+def weight_copies(case: wl.GemmCase) -> int:
+    """Copies of the quantized weights a timing rotates through: 1 when a step's working set exceeds
+    1 GiB, else enough copies for 1 GiB of weights (as consecutive layers would), at most 64."""
+    work_mb = (case.M * case.K * 2.5625 + (case.M + case.N) * case.K * 0.5625 +
+               sum(case.M * sg.n * 4 for sg in case.segments)) / 2 ** 20
+    w_mb = case.N * case.K * 0.5625 / 2 ** 20
+    return 1 if work_mb > 1024 else int(min(64, max(2, np.ceil(1024 / w_mb))))
+
+
+OTHER_CONFIGS = ("C2", "C4", "C3_up_1", "C3_up_16", "C3_up_64", "C3_down_1", "C3_down_16", "C3_down_64")
+
+
+def bench_other_configs(reps: int) -> dict:
+    """The GEMMs of the other workloads, each timed back to back over rotating weight copies (HIP
+    events on the library's stream, after a few untimed calls): prefill projection 4096x5120x5120,
+    fused MLP gate+up 8192x34816x5120, and the six decode GEMMs (HBM-bound weight streaming)."""
+    res = {}
+    for key in OTHER_CONFIGS:
+        case = wl.ALL[key]
+        step = Step(case, copies=weight_copies(case))
+        step.quantize()
+        n = max(reps, 4 * len(step.w_copies))
+        _settle(lambda i: step.gemm(), 0.1)
+        ms = _time_loop(lambda i: step.gemm(), n)
+        r = gemm_roofline(case, ms)
+        r.update({"workload": case.name, "M": case.M, "N": case.N, "K": case.K, "weight_copies": len(step.w_copies),
+                  "launches": n})
+        res[key] = r
+        log(f"[gpu] {case.name}: {ms * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s, {r['gbps']:.0f} GB/s "
+            f"({r['roofline']['bound']} {100 * r['roofline']['frac']:.1f}%)")
+        del step
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(step: Step, rows_quant: int, rows_gemm: int) -> dict:
     """The CPU oracle on a bounded sample of the same step, extrapolated linearly in M."""
     import oracle
@@ -223,12 +315,35 @@ def run_cpu_baseline(step: Step, rows_quant: int, rows_gemm: int) -> dict:
             checks[case.segments[s].name] = bool((np.abs(got - a) <= bound).all())
     codes_ok = bool((step.a_codes[:rows_quant].cpu().numpy() == a_codes).all()
                     and (step.a_scales[:rows_quant].cpu().numpy() == a_scales).all())
+    threads = oracle.num_threads()
+    # the same oracle on one thread: quantizer on 2048 rows, GEMM on 32 rows (all N), extrapolated
+    oracle.set_num_threads(1)
+    try:
+        q1_rows, g1_rows = min(2048, rows_quant), min(32, rows_gemm)
+        t0 = time.perf_counter()
+        oracle.quantize(xs[:q1_rows], g_a)
+        t_q1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_rows(a_codes, a_scales, g_a, w_codes, w_scales, bounds, g_w, rows[:g1_rows])
+        t_g1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    t_full1 = t_q1 / q1_rows * M + t_g1 / g1_rows * M
+    q_bytes_row = K * QUANT_BYTES_PER_ELEM
     return {
-        "value": 2.0 * M * N * K / t_full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "value": 2.0 * M * N * K / t_full / 1e12, "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"oracle quantize of {rows_quant} rows + exact GEMM of {rows_gemm} rows (all N) of the "
                    f"{M}x{N}x{K} step, extrapolated linearly to M={M}; measured "
                    f"{t_quant:.2f}s + {t_many:.2f}s, extrapolated full step {t_full:.1f}s"),
+        "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+        "quantize_gbps": q_bytes_row * rows_quant / t_quant / 1e9,
+        "single_thread": {
+            "value": 2.0 * M * N * K / t_full1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "quantize_gbps": q_bytes_row * q1_rows / t_q1 / 1e9,
+            "gemm_tflops": 2.0 * g1_rows * N * K / t_g1 / 1e12,
+            "sample": (f"one thread: oracle quantize of {q1_rows} rows ({t_q1:.2f}s) + exact GEMM of {g1_rows} rows "
+                       f"({t_g1:.2f}s), extrapolated to the full step: {t_full1:.0f}s")},
         "parity_sample": {"codes_scales_bit_exact": codes_ok, **checks},
     }
 
@@ -510,6 +625,8 @@ def main() -> int:
                     help="overwrite a buffer of this size before each step (-1: none)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other configurations' GEMM timings (profiling runs)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch.matmul (hipBLASLt) on dense FP16 and BF16 operands of the same "
                          "shape, alternating with the NVFP4 GEMM in this process")
@@ -531,10 +648,7 @@ def main() -> int:
     case = wl.ALL[args.workload]
     # a step whose working set fits the 256 MB last-level cache would be served from it: such steps
     # rotate through copies of the weights, 1 GiB in all
-    work_mb = (case.M * case.K * 2.5625 + (case.M + case.N) * case.K * 0.5625 +
-               sum(case.M * sg.n * 4 for sg in case.segments)) / 2 ** 20
-    w_mb = case.N * case.K * 0.5625 / 2 ** 20
-    copies = 1 if work_mb > 1024 else int(min(64, max(2, np.ceil(1024 / w_mb))))
+    copies = weight_copies(case)
     step = Step(case, copies=copies)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -553,13 +667,16 @@ def main() -> int:
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     q_bytes = QUANT_BYTES_PER_ELEM * M * K
-    q_gbps = q_bytes / (r["quant_iso_ms"] * 1e-3) / 1e9
+    qrot = time_quantizer_rotating(step)
+    q_gbps = q_bytes / (qrot["ms"] * 1e-3) / 1e9
+    q_gbps_same_x = q_bytes / (r["quant_iso_ms"] * 1e-3) / 1e9
     out_bytes = sum(M * s.n * (4 if s.out_dtype == wl.OUT_F32 else 2) for s in case.segments)
     gemm_bytes = 0.5625 * (M + N) * K + out_bytes  # codes + scales of A and W, plus the outputs
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     # the GEMM's bound: dense FP16 MFMA above the ridge point (peak FLOP/s per HBM byte/s), HBM below
     mfma_bound = flops / gemm_bytes >= PEAK_F16_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {r['quant_iso_ms']:.3f} ms ({q_gbps:.0f} GB/s), "
+    log(f"[gpu] step {r['step_ms']:.3f} ms: quantize {qrot['ms']:.4f} ms over {qrot['copies']} rotating inputs "
+        f"({q_gbps:.0f} GB/s; {q_gbps_same_x:.0f} GB/s on one input), "
         f"gemm {gemm_ms:.4f} ms ({gemm_tflops:.0f} TFLOP/s, {gemm_gbps:.0f} GB/s), weight copies {copies}")
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
@@ -600,15 +717,22 @@ def main() -> int:
         "roofline_quantize": {"bound": "hbm", "achieved": q_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                               "frac": q_gbps / PEAK_HBM_GBPS, "traffic": trq[0] if trq else None,
                               "traffic_detail": trq[1] if trq else None, "kernel": "quantize_kernel",
-                              "avg_ms": r["quant_iso_ms"], "avg_ms_in_step": r["quant_ms"],
+                              "avg_ms": qrot["ms"], "rotation": {k: v for k, v in qrot.items() if k != "ms"},
+                              "avg_ms_one_input": r["quant_iso_ms"], "avg_ms_in_step": r["quant_ms"],
                               "algorithmic_bytes": q_bytes, "copy_ceiling_gbps": copy_gbps,
                               "frac_of_copy_ceiling": q_gbps / copy_gbps},
     }
+
     if args.library_gemm:
         out["library_gemm"] = library_gemm(step, M, N, K)
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle on a sample")
         out["cpu_baseline"] = run_cpu_baseline(step, min(args.cpu_rows_quant, M), min(args.cpu_rows_gemm, M))
+    if not args.no_extras and args.workload == "C5":
+        del step
+        torch.cuda.empty_cache()
+        log("[gpu] other configurations")
+        out["other_configs"] = bench_other_configs(max(args.steps, 20))
     print(json.dumps(out), flush=True)
     return 0
 

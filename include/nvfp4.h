@@ -132,7 +132,8 @@ typedef struct {
  *   every row stride is below 2^23 bytes (so K < 2^24 for dense codes), else SHAPE;
  *   segs[n_segs]: host array, sorted by n_begin, contiguous, non-overlapping, covering [0, N),
  *                 every n_len > 0, 1 <= n_segs <= NVFP4_MAX_SEGMENTS;
- *   g_w[n_segs]: host array, the weight global scale of each segment (finite, > 0).
+ *   g_w[n_segs]: host array, the weight global scale of each segment (finite, > 0); each
+ *                product RN32(g_a * g_w[s]) must be a normal positive float, else SCALE.
  * The product of the decoded operands is accumulated in FP32 from exact FP16 products (an E2M1
  * value times an E4M3 scale is exact in FP16), then scaled once by RN32(g_a * g_w[s]).
  * M == 0 or N == 0 is a no-op; K == 0 writes the epilogue of y = 0.
@@ -210,6 +211,8 @@ nvfp4_status nvfp4_fold_scales(uint8_t* scales, int64_t rows, int64_t nblocks, i
  * nvfp4_fold_scales of module s's rows with r_s. Writes G to the host pointer g_common. Afterwards
  * the group runs as one GEMM segment with global scale G (codes are unchanged).
  *   w_scales: device uint8 [N, K/16], stride ldw_s bytes; K a multiple of 16.
+ * Every argument (including each ratio, which must not underflow to 0) is validated before
+ * anything is written or enqueued, so an error leaves the scales and *g_common untouched.
  * Errors: NULL, SHAPE, SEGMENTS, SCALE, HIP.
  */
 nvfp4_status nvfp4_fold_group(uint8_t* w_scales, int64_t ldw_s, int64_t K, const int64_t* seg_rows,
@@ -233,8 +236,9 @@ nvfp4_status nvfp4_rmsnorm_quantize(const void* x_bf16, int64_t rows, int64_t K,
                                     uint8_t* scales, int64_t lds, void* y_bf16, int64_t ldy,
                                     void* stream);
 
-/* Static English name of a status code. */
-const char* nvfp4_status_string(nvfp4_status s);
+/* Static English name of a status code (any int: values that are no nvfp4_status give
+ * "unknown status"). */
+const char* nvfp4_status_string(int status);
 
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char* nvfp4_last_error(void);

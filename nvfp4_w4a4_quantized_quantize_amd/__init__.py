@@ -6,8 +6,9 @@ include/nvfp4.h (nvfp4_global_scale, nvfp4_quantize, nvfp4_gemm, and the serving
 nvfp4_kv_scale / nvfp4_kv_quantize / nvfp4_kv_dequantize, nvfp4_fold_scales / nvfp4_fold_group,
 nvfp4_rmsnorm_quantize, nvfp4_gdn_recurrence).
 
-If the library has not been built (``python -m nvfp4_w4a4_quantized_quantize_amd.build``), every
-call raises: there is no fallback implementation.
+If the library has not been built (``python -m nvfp4_w4a4_quantized_quantize_amd.build``), or was
+built from sources other than the ones in the tree, every call raises: there is no fallback
+implementation.
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+# NVFP4_LIB names another build of the same sources (the host-sanitizer run uses it).
+LIB_PATH = os.environ.get("NVFP4_LIB") or os.path.join(_PKG, "libnvfp4.so")
 
 OK = 0
 OUT_F32, OUT_BF16 = 0, 1
@@ -53,8 +55,12 @@ def lib() -> ctypes.CDLL:
     """Load libnvfp4.so (raises if it is missing: the path has no fallback)."""
     global _lib
     if _lib is None:
+        from . import build as _build
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run python -m nvfp4_w4a4_quantized_quantize_amd.build")
+        if not _build.built_from_current_sources(LIB_PATH, _build.sources()):
+            raise ImportError(f"{LIB_PATH} was built from other sources than the ones in the tree; rebuild it "
+                              "with python -m nvfp4_w4a4_quantized_quantize_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, f32, P = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
         L.nvfp4_global_scale.restype = i32
@@ -173,17 +179,7 @@ class Segment:
     out: Optional[torch.Tensor] = None      # preallocated [M, n] output (optional)
 
 
-def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: torch.Tensor,
-         w_scales: torch.Tensor, segments: Sequence[Segment], workspace: Optional[torch.Tensor] = None,
-         stream=None) -> list[torch.Tensor]:
-    """Block-scaled W4A4 GEMM Y = A W^T with one global scale per output segment.
-
-    a_codes [M, K/2], a_scales [M, K/16]; w_codes [N, K/2], w_scales [N, K/16] (uint8, device).
-    Returns one output tensor [M, n_s] per segment.
-    """
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
-    assert w_codes.shape[1] * 2 == K and a_scales.shape == (M, K // 16) and w_scales.shape == (N, K // 16)
+def _segments(a_codes: torch.Tensor, M: int, N: int, segments: Sequence[Segment]):
     assert sum(s.n for s in segments) == N, "segments must cover N"
     n_segs = len(segments)
     segs = (_Segment * max(n_segs, 1))()
@@ -199,6 +195,21 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: tor
         g_w[i] = float(s.g_w)
         outs.append(out)
         begin += s.n
+    return segs, g_w, n_segs, outs
+
+
+def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: torch.Tensor,
+         w_scales: torch.Tensor, segments: Sequence[Segment], workspace: Optional[torch.Tensor] = None,
+         stream=None) -> list[torch.Tensor]:
+    """Block-scaled W4A4 GEMM Y = A W^T with one global scale per output segment.
+
+    a_codes [M, K/2], a_scales [M, K/16]; w_codes [N, K/2], w_scales [N, K/16] (uint8, device).
+    Returns one output tensor [M, n_s] per segment.
+    """
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    assert w_codes.shape[1] * 2 == K and a_scales.shape == (M, K // 16) and w_scales.shape == (N, K // 16)
+    segs, g_w, n_segs, outs = _segments(a_codes, M, N, segments)
     need = lib().nvfp4_gemm_workspace_bytes(M, N, K)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)

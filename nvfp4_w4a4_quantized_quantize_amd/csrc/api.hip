@@ -62,8 +62,8 @@ nvfp4_status check_nvfp4(const uint8_t* codes, int64_t ldc, const uint8_t* scale
 
 extern "C" {
 
-const char* nvfp4_status_string(nvfp4_status s) {
-    switch (s) {
+const char* nvfp4_status_string(int status) {
+    switch (status) {
         case NVFP4_OK: return "ok";
         case NVFP4_ERR_NULL: return "null pointer";
         case NVFP4_ERR_SHAPE: return "invalid shape or stride";
@@ -160,6 +160,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
         sp.n_begin[s] = sg.n_begin;
         sp.n_end[s] = expect;
         sp.scale[s] = g_a * g_w[s];  // RN32(g_a * g_w[s])
+        if (!std::isnormal(sp.scale[s]))
+            return fail(NVFP4_ERR_SCALE, "segment %d: g_a * g_w = %g * %g = %g is not a normal positive float", s,
+                        (double)g_a, (double)g_w[s], (double)sp.scale[s]);
         sp.epilogue[s] = sg.epilogue;
         sp.out_dtype[s] = sg.out_dtype;
         sp.out[s] = sg.out;
@@ -262,18 +265,34 @@ nvfp4_status nvfp4_fold_group(uint8_t* w_scales, int64_t ldw_s, int64_t K, const
     if (K < 0 || K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a non-negative multiple of 16", (long long)K);
     if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
         return fail(NVFP4_ERR_SEGMENTS, "n_segs = %d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);
+    // pass 1: validate everything (rows, scales, every ratio, the scale buffer) before touching any
+    // output, so that an error leaves the weights and *g_common as they were
     float G = 0.0f;
+    int64_t total_rows = 0;
     for (int s = 0; s < n_segs; ++s) {
         if (seg_rows[s] < 0) return fail(NVFP4_ERR_SEGMENTS, "segment %d has %lld rows", s, (long long)seg_rows[s]);
         if (!good_scale(g_w[s])) return fail(NVFP4_ERR_SCALE, "g_w[%d] = %g must be finite and > 0", s, (double)g_w[s]);
         if (g_w[s] > G) G = g_w[s];
+        total_rows += seg_rows[s];
     }
+    float ratio[NVFP4_MAX_SEGMENTS];
+    for (int s = 0; s < n_segs; ++s) {
+        ratio[s] = g_w[s] / G;  // RN32
+        if (!good_scale(ratio[s]))
+            return fail(NVFP4_ERR_SCALE, "ratio g_w[%d] / G = %g / %g underflows to 0", s, (double)g_w[s], (double)G);
+    }
+    const int64_t nblocks = K / 16;
+    if (total_rows > 0 && nblocks > 0) {
+        if (!w_scales) return fail(NVFP4_ERR_NULL, "w_scales is NULL");
+        if (ldw_s < nblocks)
+            return fail(NVFP4_ERR_SHAPE, "row stride %lld < nblocks = %lld", (long long)ldw_s, (long long)nblocks);
+    }
+    // pass 2: every argument is valid; enqueue the folds
     *g_common = G;
     int64_t row0 = 0;
     for (int s = 0; s < n_segs; ++s) {
-        const float ratio = g_w[s] / G;  // RN32
-        nvfp4_status st = nvfp4_fold_scales(w_scales + row0 * ldw_s, seg_rows[s], K / 16, ldw_s, ratio, stream);
-        if (st != NVFP4_OK) return st;
+        nvfp4_status st = nvfp4_fold_scales(w_scales + row0 * ldw_s, seg_rows[s], nblocks, ldw_s, ratio[s], stream);
+        if (st != NVFP4_OK) return st;  // only a launch failure can remain here
         row0 += seg_rows[s];
     }
     return ok();

@@ -27,7 +27,6 @@
 //  * The KW partial sums meet in LDS and are added in wave order (deterministic), then scaled by
 //    g_a * g_w of the column's segment, gated and stored, consecutive threads on consecutive columns.
 #include <algorithm>
-#include <atomic>
 
 #include "device_common.h"
 
@@ -553,16 +552,13 @@ struct WideShape {
     int rows, wpg, nt;
 };
 
-// CUs of the current device, read once per device (concurrent first calls store the same value).
+// CUs of the current device (a host query of the device's properties; it neither allocates nor
+// synchronizes).
 static int device_cus() {
-    static std::atomic<int> cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev].store(n, std::memory_order_relaxed);
-    }
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
     return n;
 }
 

@@ -31,6 +31,28 @@ __device__ __forceinline__ uint32_t put_e2m1_pair(uint32_t word, float lo, float
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lo, hi, 1.0f, sel);
 }
 
+// RN32(a / S) for a = |x| of a bf16 value and S > 0, given y = rcp(S):
+//   q0 = a y;  r = fma(-q0, S, a);  q1 = fma(r, y, q0).
+// Inside quotient_fast_ok's range the residual r is exact whenever the quotient is at least 2^-11
+// (the products' granularity ulp(q0) ulp(S) stays above the smallest subnormal), and q1 is then the
+// correctly rounded quotient. Below 2^-11 the residual can underflow and q1 may differ from the IEEE
+// quotient in its last bits, but both stay below 2^-10, where every E2M1 code and every E4M3 byte is
+// zero. The self-test module checks both statements on the device for every bf16 numerator against
+// every binary32 significand of S, in divisor binades across the range. A zero y gives 0 (the
+// encoder's zero-scale block).
+__device__ __forceinline__ float quotient_fast(float a, float S, float y) {
+    const float q0 = a * y;
+    const float r = __builtin_fmaf(-q0, S, a);
+    return __builtin_fmaf(r, y, q0);
+}
+
+// Divisors for which quotient_fast is used: S in [2^-80, 2^100] (S and 1/S normal, and a quotient of
+// 2^-11 or more implies a numerator large enough for an exact residual).
+__device__ __forceinline__ bool divisor_fast_ok(float S) { return S >= 0x1p-80f && S <= 0x1p100f; }
+
+// The whole range: a fast divisor and a quotient below 2^100.
+__device__ __forceinline__ bool quotient_fast_ok(float S, float a) { return divisor_fast_ok(S) && a * 0x1p-100f <= S; }
+
 struct Block16 {
     uint32_t c0, c1;  // 16 packed codes, element 2i in the low nibble of byte i
     uint32_t sb;      // E4M3 scale byte
@@ -50,24 +72,15 @@ __device__ __forceinline__ Block16 encode_block16(const float (&f)[16], float g)
     const float s = e4m3_to_f32(sb);
     const float S = s * g;
 
-    // v = RN32(|x| / S). Fast path: y = rcp(S) then one exact-residual correction
-    //   q0 = |x| y;  r = fma(-q0, S, |x|) (exact);  q1 = fma(r, y, q0)
-    // which equals the correctly rounded quotient for bf16 |x| whenever S, 1/S and the quotient
-    // stay inside the normal range (checked against IEEE division for every bf16 significand and
-    // every binary32 significand of S). A zero scale takes y = 0, giving q1 = 0. Blocks outside
-    // that range (extreme global scales) use the IEEE division.
-    const bool fast = (s == 0.0f) || (S >= 0x1p-100f && S <= 0x1p100f && amax * 0x1p-100f <= S);
+    // v = RN32(|x| / S) by quotient_fast inside its range (every |x| of the block is <= amax); a zero
+    // scale takes y = 0, giving v = 0. Blocks outside the range (extreme global scales) use the IEEE
+    // division.
+    const bool fast = (s == 0.0f) || quotient_fast_ok(S, amax);
     float v[16];
     if (fast) {
         const float y = (s == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(S);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float a = fabsf(f[i]);
-            const float q0 = a * y;
-            const float r = __builtin_fmaf(-q0, S, a);
-            const float q1 = __builtin_fmaf(r, y, q0);
-            v[i] = __builtin_copysignf(q1, f[i]);
-        }
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(quotient_fast(fabsf(f[i]), S, y), f[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(__fdiv_rn(fabsf(f[i]), S), f[i]);

@@ -15,15 +15,11 @@
 namespace nvfp4 {
 namespace {
 
-// RN32(a / S) for a = |x| of a bf16 value, S > 0: the reciprocal with one exact-residual correction
-// is the correctly rounded quotient while S, 1/S and the quotient stay in the normal range (the
-// condition the NVFP4 block encoder uses); otherwise the IEEE division.
+// RN32(a / S) for a = |x| of a bf16 value, S > 0: quotient_fast (the reciprocal with one
+// exact-residual correction) inside its range, where it gives the same E4M3 byte as the correctly
+// rounded quotient, else the IEEE division.
 __device__ __forceinline__ float quotient_rn(float a, float S, float y, bool s_ok) {
-    if (s_ok && a * 0x1p-100f <= S) {
-        const float q0 = a * y;
-        const float r = __builtin_fmaf(-q0, S, a);
-        return __builtin_fmaf(r, y, q0);
-    }
+    if (s_ok && a * 0x1p-100f <= S) return quotient_fast(a, S, y);
     return __fdiv_rn(a, S);
 }
 
@@ -51,7 +47,7 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
     const qu32x4* src = reinterpret_cast<const qu32x4*>(x + (int64_t)row * ldx + 16u * u);
     const qu32x4 p0 = __builtin_nontemporal_load(src), p1 = __builtin_nontemporal_load(src + 1);
     const float y = __builtin_amdgcn_rcpf(s);
-    const bool s_ok = s >= 0x1p-100f && s <= 0x1p100f;
+    const bool s_ok = divisor_fast_ok(s);
     qu32x4 o;
     o[0] = kv_pair(p0[0], s, y, s_ok) | (kv_pair(p0[1], s, y, s_ok) << 16);
     o[1] = kv_pair(p0[2], s, y, s_ok) | (kv_pair(p0[3], s, y, s_ok) << 16);

@@ -17,7 +17,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_LIB names another build of the same source (the host-sanitizer run uses it).
+_LIB = os.environ.get("NVFP4_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 # -ffp-contract=off: no fused multiply-add, so each binary32 step rounds once, as the spec states.
 CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11",
@@ -39,7 +40,8 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.environ.get("NVFP4_ORACLE_LIB") and (not os.path.exists(_LIB) or
+                                                        os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         L = ctypes.CDLL(_LIB)
         i64, f32, f64, i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_int
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_from_float_array.argtypes = [P, i64, P]
         L.oracle_num_threads.restype = i32
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_e2m1_from_float_array.restype = None
         L.oracle_e2m1_from_float_array.argtypes = [P, i64, P]
         L.oracle_kv_scale.restype = f32
@@ -104,6 +108,11 @@ def lib() -> ctypes.CDLL:
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later OpenMP row loops (the CPU-baseline timing also runs the oracle on one)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

@@ -485,3 +485,13 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Sets the number of threads later OpenMP row loops use (n >= 1; ignored without OpenMP). Only the
+ * CPU-baseline timing uses it, to time the oracle single-threaded as well. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -64,7 +64,7 @@ def check_decay(gpu: np.ndarray, y: np.ndarray, T: np.ndarray, oracle_alpha: np.
                 a_log: np.ndarray, dt_bias: np.ndarray) -> None:
     a = oracle_alpha
     z = y + dt_bias.astype(np.float64)[None, :]
-    sig = 1.0 / (1.0 + np.exp(-z))
+    sig = np.exp(-np.logaddexp(0.0, -z))  # logistic(z) without overflow for large |z|
     ln_a = np.log(np.maximum(a, 1e-300))
     bound = a * np.exp(a_log.astype(np.float64))[None, :] * sig * tol_fp32(T) + 2.0 ** -20 * a * (1 + np.abs(ln_a)) + 2.0 ** -126
     bad = np.abs(gpu.astype(np.float64) - a) > bound

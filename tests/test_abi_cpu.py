@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def L():
-    if not os.path.exists(nv.LIB_PATH):
+    if hipbuild.stale():
         hipbuild.build()
     return nv.lib()
 
@@ -101,6 +101,8 @@ def g(L, M=8, N=64, K=64, segs=None, g_w=None, n_segs=None, g_a=1.0, a_codes=A16
     (dict(segs=[(0, 32, 0, 0, A16, 64, None, None), (40, 24, 0, 0, A16, 64, None, None)]), 4),
     (dict(segs=[(0, 0, 0, 0, A16, 64, None, None), (0, 64, 0, 0, A16, 64, None, None)]), 4),
     (dict(g_a=0.0), 5), (dict(g_w=[float("nan")]), 5), (dict(g_w=[-2.0]), 5),
+    # RN32(g_a * g_w) overflowing to inf, or underflowing to a subnormal or zero
+    (dict(g_a=1e30, g_w=[1e30]), 5), (dict(g_a=1e-30, g_w=[1e-30]), 5), (dict(g_a=1e-20, g_w=[1e-20]), 5),
     (dict(segs=[(0, 64, 3, 0, A16, 64, None, None)]), 6),
     (dict(segs=[(0, 64, 0, 2, A16, 64, None, None)]), 6),
     (dict(segs=[(0, 64, 1, 1, A16, 64, None, None)]), 6),
@@ -200,6 +202,15 @@ def test_fold_rejects(L):
     bad = (ctypes.c_float * 2)(0.5, float("nan"))
     assert L.nvfp4_fold_group(A16, 16, 64, rows, bad, 2, ctypes.byref(G), None) == 5
     assert L.nvfp4_fold_group(A16, 16, 64, rows, gw, 2, None, None) == 1
+    # a ratio g_w[s] / max g_w that underflows to 0 is rejected before anything is written: g_common
+    # keeps its value (and no fold of an earlier segment is enqueued; the scale pointer is fake here)
+    G.value = -7.0
+    tiny = (ctypes.c_float * 2)(3e38, 1e-45)  # the second segment's ratio underflows
+    assert L.nvfp4_fold_group(A16, 16, 64, rows, tiny, 2, ctypes.byref(G), None) == 5
+    assert G.value == -7.0
+    assert L.nvfp4_fold_group(None, 16, 64, rows, gw, 2, ctypes.byref(G), None) == 1
+    assert L.nvfp4_fold_group(A16, 2, 64, rows, gw, 2, ctypes.byref(G), None) == 2
+    assert G.value == -7.0
 
 
 def rq(L, x=A16, rows=4, K=64, ldx=64, w=A16, eps=1e-6, g=1.0, codes=A16, ldc=32, scales=A16, lds=16, y=None,
@@ -250,3 +261,4 @@ def test_gdn_rejects(L, kw, status):
 def test_gdn_empty_and_token_by_token_need_no_workspace(L):
     assert gdn(L, B=0, ws=None, ws_bytes=0) == 0
     assert gdn(L, T=0, ws=None, ws_bytes=0) == 0
+

@@ -1,8 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
 The whole activation tensor is quantized on the GPU and compared with the oracle bit for bit; the
-GEMM is compared with the oracle's exact result on sampled rows across all N columns: one seeded
-row per 128-row M tile, the first and last rows, and the rows holding the largest activations.
+GEMM is compared with the oracle's exact result on every output of the single prefill projection
+(4096 x 5120 x 5120, in FP32 and bf16), and on sampled rows across all N columns of the larger fused
+GEMMs: one seeded row per 128-row M tile, the first and last rows, and the rows holding the largest
+activations.
 Every input is drawn by the seeded workload generator; g is calibrated on the GPU and checked
 against the oracle's value.
 """
@@ -34,7 +36,7 @@ def sample_rows(x_bits: np.ndarray, M: int, seed: int) -> np.ndarray:
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def run_case(case: wl.GemmCase, out_dtype_plain, check_unfused: bool):
+def run_case(case: wl.GemmCase, out_dtype_plain, check_unfused: bool, all_rows: bool = False):
     print(f"{case.name}: drawing inputs", flush=True)
     x = wl.draw_x(case)
     xd = dev_bf16(x)
@@ -70,7 +72,7 @@ def run_case(case: wl.GemmCase, out_dtype_plain, check_unfused: bool):
     assert (host(wc) == rw_c).all() and (host(ws) == rw_s).all(), "weight codes/scales differ"
     print(f"{case.name}: GEMM {case.M}x{N}x{K}", flush=True)
     outs = nv.gemm(ac, as_, g_a, wc, ws, segs)
-    rows = sample_rows(x, case.M, case.cfg_id)
+    rows = np.arange(case.M, dtype=np.int64) if all_rows else sample_rows(x, case.M, case.cfg_id)
     y, T = oracle.gemm_rows(rac, ras, g_a, rw_c, rw_s, case.seg_bounds, np.array(g_w, np.float32), rows)
     rows_t = torch.from_numpy(rows).to(DEV)
     worst = 0.0
@@ -87,7 +89,8 @@ def run_case(case: wl.GemmCase, out_dtype_plain, check_unfused: bool):
             worst = max(worst, check_fp32(host(got), ys, Ts, f"{case.name} {seg.name}"))
         else:
             check_bf16(got, ys, Ts, f"{case.name} {seg.name}")
-    print(f"{case.name}: {len(rows)} sampled rows within tolerance (max |err|/T {worst:.3g})", flush=True)
+    print(f"{case.name}: {len(rows)} {'(all)' if all_rows else 'sampled'} rows within tolerance "
+          f"(max |err|/T {worst:.3g})", flush=True)
     if check_unfused:
         # each module alone gives bitwise the same columns as the fused GEMM
         n0 = 0
@@ -96,15 +99,32 @@ def run_case(case: wl.GemmCase, out_dtype_plain, check_unfused: bool):
             (u,) = nv.gemm(ac, as_, g_a, wc[n0:n0 + seg.n], ws[n0:n0 + seg.n], [alone])
             assert torch.equal(u, outs[s]), f"{case.name}: segment {seg.name} fused != unfused"
             n0 += seg.n
+    return dict(ac=ac, as_=as_, wc=wc, ws=ws, g_a=g_a, g_w=g_w, rows=rows, y=y, T=T, outs=outs)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_projection(dtype):
-    run_case(wl.C2, dtype, check_unfused=False)
+    """Every one of the 4096 x 5120 outputs against the oracle's exact result."""
+    run_case(wl.C2, dtype, check_unfused=False, all_rows=True)
 
 
 def test_fused_mlp_gate_up():
-    run_case(wl.C4, torch.float32, check_unfused=True)
+    """The fused gate+up GEMM at full size, then the pages' fused-module trap ("Trap 1") on the same
+    operands: one global scale (the first module's) for both modules mis-scales every output of the
+    second module by g_w1 / g_w2, a relative error of |1 - g_w1 / g_w2| (about 0.67 here, the size of
+    the pages' 0.35 / 0.57), while the first module stays within the FP32 bound."""
+    case = wl.C4
+    r = run_case(case, torch.float32, check_unfused=True)
+    n1 = case.segments[0].n
+    g1, g2 = r["g_w"]
+    (bad,) = nv.gemm(r["ac"], r["as_"], r["g_a"], r["wc"], r["ws"], [nv.Segment(case.N, g1)])
+    got = host(bad.index_select(0, torch.from_numpy(r["rows"]).to(DEV))).astype(np.float64)
+    y, T = r["y"], r["T"]
+    check_fp32(got[:, :n1], y[:, :n1], T[:, :n1], "first module under its own scale")
+    rel = np.abs(got[:, n1:] - y[:, n1:]).sum() / np.abs(y[:, n1:]).sum()
+    expect = abs(1.0 - float(g1) / float(g2))
+    print(f"single global scale: second module relative error {rel:.4f} (expected {expect:.4f})", flush=True)
+    assert expect > 0.3 and abs(rel - expect) < 1e-4 * expect
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

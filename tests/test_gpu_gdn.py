@@ -173,3 +173,31 @@ def test_prefill_8192_tokens_all_heads():
     o, S = run_gpu(q, k, v, a, b, 1, 8192, 32)
     rel = check(o, S, q, k, v, a, b, 1, 8192, what="prefill 8192")
     print(f"prefill 8192: max |o - exact| / max |o| = {rel:.3g}")
+
+
+def test_prefill_32768_tokens_all_heads():
+    """The 32768-token prefill the companion benchmark times (same seeded inputs), every token, head
+    and state entry against the double oracle; on top of the global bound, no stretch of the sequence
+    may be worse than 8 times the float32 twin's error over a window of 512 tokens around it."""
+    case = wl.GDN_PREFILL
+    q, k, v, a, b = wl.draw_gdn(case)
+    T = case.T
+    print(f"{case.name}: GPU", flush=True)
+    o, S = run_gpu(q, k, v, a, b, 1, T, case.Hv)
+    print(f"{case.name}: oracle (double and float32 twin)", flush=True)
+    o64, S64 = oracle.gdn_recurrence(q, k, v, a, b, 1, T)
+    o32, S32 = oracle.gdn_recurrence(q, k, v, a, b, 1, T, f32=True)
+    for got, ref, twin, name in ((o, o64, o32, "o"), (S, S64, S32, "state")):
+        tol = 8 * np.abs(twin - ref).max() + 2.0 ** -22 * np.abs(ref).max()
+        err = np.abs(got - ref).max()
+        assert err <= tol, f"prefill 32768 {name}: max error {err:.3g} > tolerance {tol:.3g}"
+    floor = 2.0 ** -22 * np.abs(o64).max()
+    err_t = np.abs(o - o64).max(axis=1)
+    twin_t = np.abs(o32 - o64).max(axis=1)
+    win = 512
+    pad = np.concatenate([np.zeros(win // 2), twin_t, np.zeros(win // 2)])
+    local = np.lib.stride_tricks.sliding_window_view(pad, win)[:T].max(axis=1)
+    bad = np.nonzero(err_t > 8 * local + floor)[0]
+    assert bad.size == 0, f"tokens {bad[:8]} exceed 8x the local float32 error"
+    rel = np.abs(o - o64).max() / np.abs(o64).max()
+    print(f"prefill 32768: max |o - exact| / max |o| = {rel:.3g}", flush=True)

@@ -106,7 +106,8 @@ def _grid_blocks(g: float) -> np.ndarray:
     return out.reshape(-1, 64 * 16)
 
 
-@pytest.mark.parametrize("g", [2.0 ** -6, 0.0173, 1.0 / 3.0, 3.14159e-3, 7.77e-8, 12.34])
+# the last two put block scales s * g on both sides of the fast division's lower edge (2^-80)
+@pytest.mark.parametrize("g", [2.0 ** -6, 0.0173, 1.0 / 3.0, 3.14159e-3, 7.77e-8, 12.34, 2.0 ** -85, 3.7e-26])
 def test_every_bf16_value_over_scale_grid(g):
     g = np.float32(g)
     bits = _grid_blocks(float(g))

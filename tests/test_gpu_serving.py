@@ -42,7 +42,7 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 # ------------------------------------------------------------------ FP8 KV codec
 @pytest.mark.parametrize("rows,cols,strided", [(1, 16, False), (3, 144, True), (257, 1024, False),
                                                (64, 128, True), (4096, 1024, False), (1, 48, False)])
-@pytest.mark.parametrize("s", [0.0123, 2.0 ** -110, 3.0e30])
+@pytest.mark.parametrize("s", [0.0123, 2.0 ** -110, 2.0 ** -85, 2.0 ** -79, 3.0e30])
 def test_kv_quantize_bit_exact(rows, cols, strided, s):
     rng = np.random.default_rng(rows * 31 + cols)
     x = specials_mixed(rng, rows, cols, spread=8.0 if s < 1 else 40.0)

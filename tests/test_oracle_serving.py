@@ -202,3 +202,24 @@ def test_rmsnorm_r_from_exactly_rounded_sum_and_unit_rms():
     yv = bf16_vals(y).astype(np.float64)
     ms_rows = (xv * xv).mean(axis=1)
     assert np.allclose((yv * yv).mean(axis=1), ms_rows / (ms_rows + float(eps)), rtol=2.0 ** -7)
+
+
+def test_rmsnorm_rounding_order_matches_torch_bf16_arithmetic():
+    """The two bf16 roundings of the norm's output, y = bf16(w * bf16(x * r)), against PyTorch's own
+    CPU arithmetic: a float32 product x * r, a cast to bf16 and a bf16 x bf16 multiply (which torch
+    rounds to bf16 once). Given the oracle's r (pinned above by the exactly rounded sum), every
+    output must agree bit for bit. The rows are chosen so that a single rounding of x * r * w gives a
+    different answer on some elements, so the pin tells the two readings apart."""
+    import torch
+    rng = np.random.default_rng(31)
+    K = 1024
+    x = bf16_bits(rng.standard_normal((16, K)) * np.exp(rng.uniform(-3, 3, (16, 1))))
+    w = bf16_bits(rng.uniform(0.3, 2.7, K))
+    y, r = oracle.rmsnorm(x, w, np.float32(1e-6))
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+    rt = torch.from_numpy(r)[:, None]
+    ref = (wt[None, :] * (xt * rt).to(torch.bfloat16)).view(torch.int16).numpy().view(np.uint16)
+    assert (y == ref).all()
+    once = ((xt * rt) * wt.float()[None, :]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (once != y).sum() > 100, "the sample does not separate one rounding from two"
