@@ -70,6 +70,7 @@ typedef enum {
 enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
 enum { NVFP4_EPI_NONE = 0, NVFP4_EPI_SIGMOID = 1, NVFP4_EPI_GDN_DECAY = 2 };
 enum { NVFP4_MAX_SEGMENTS = 16 };
+enum { NVFP4_NOALLOC_SCRATCH_BYTES = 16 << 20 }; /* scratch of nvfp4_gemm_noalloc, per GPU */
 
 /*
  * nvfp4_global_scale -- calibration of a module's FP32 global scale from a bf16 tensor:
@@ -153,6 +154,24 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
  * n = ceil(K / 256) chunks: s0 = min(8, max(1, n / 11)), p = ceil(n / s0) rounded up to even,
  * splits = ceil(n / p); the size is splits * N * 64 * 4 when splits > 1, else 0. */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * nvfp4_gemm_noalloc -- nvfp4_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments (without the
+ * workspace), same kernels and bitwise the same results as nvfp4_gemm. The call allocates nothing:
+ * where nvfp4_gemm would use the caller's workspace (the decode kernel's split-K partial sums,
+ * 32 < M <= 64 with K split), it uses a static device array of NVFP4_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * that the library holds on every GPU it runs on until the process ends. A shape whose
+ * nvfp4_gemm_workspace_bytes() exceeds that returns NVFP4_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array (its contents carry over between calls and need no
+ * clearing: each call writes every partial sum it reads), so calls that may overlap on one GPU --
+ * different streams, or host threads not ordered on one stream -- race and must be serialized by
+ * the caller. Errors: as nvfp4_gemm.
+ */
+nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales,
+                                int64_t lda_s, float g_a, const uint8_t* w_codes, int64_t ldw_c,
+                                const uint8_t* w_scales, int64_t ldw_s, int64_t M, int64_t N, int64_t K,
+                                const nvfp4_segment* segs, const float* g_w, int32_t n_segs, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Companions on the same serving path

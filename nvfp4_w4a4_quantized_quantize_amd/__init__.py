@@ -33,7 +33,8 @@ _EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
 EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
             "nvfp4_status_string", "nvfp4_last_error", "nvfp4_kv_scale", "nvfp4_kv_quantize",
             "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize",
-            "nvfp4_gdn_recurrence", "nvfp4_gdn_workspace_bytes")
+            "nvfp4_gdn_recurrence", "nvfp4_gdn_workspace_bytes", "nvfp4_gemm_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Nvfp4Error(RuntimeError):
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm.restype = i32
         L.nvfp4_gemm.argtypes = [P, i64, P, i64, f32, P, i64, P, i64, i64, i64, i64,
                                  ctypes.POINTER(_Segment), ctypes.POINTER(f32), i32, P, ctypes.c_size_t, P]
+        L.nvfp4_gemm_noalloc.restype = i32
+        L.nvfp4_gemm_noalloc.argtypes = [P, i64, P, i64, f32, P, i64, P, i64, i64, i64, i64,
+                                         ctypes.POINTER(_Segment), ctypes.POINTER(f32), i32, P]
         L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -217,6 +221,20 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: tor
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ld(a_codes, 16), _ptr(a_scales), _ld(a_scales, 16), float(g_a),
                             _ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), M, N, K,
                             segs, g_w, n_segs, _ptr(workspace), ws_bytes, _stream(stream)), "nvfp4_gemm")
+    return outs
+
+
+def gemm_noalloc(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: torch.Tensor,
+                 w_scales: torch.Tensor, segments: Sequence[Segment], stream=None) -> list[torch.Tensor]:
+    """gemm() through nvfp4_gemm_noalloc: the library allocates nothing (its partial sums use a fixed
+    per-GPU scratch array). Outputs are allocated here unless every segment brings its own `out`."""
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    assert w_codes.shape[1] * 2 == K and a_scales.shape == (M, K // 16) and w_scales.shape == (N, K // 16)
+    segs, g_w, n_segs, outs = _segments(a_codes, M, N, segments)
+    _check(lib().nvfp4_gemm_noalloc(_ptr(a_codes), _ld(a_codes, 16), _ptr(a_scales), _ld(a_scales, 16), float(g_a),
+                                    _ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), M, N, K,
+                                    segs, g_w, n_segs, _stream(stream)), "nvfp4_gemm_noalloc")
     return outs
 
 

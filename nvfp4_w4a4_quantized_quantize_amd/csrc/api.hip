@@ -3,10 +3,40 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "internal.h"
 
 namespace {
+
+// Scratch of nvfp4_gemm_noalloc: the decode kernel's split-K partial sums, for callers that cannot
+// allocate. Each GPU the library runs on holds its own copy from module load until the process
+// ends. In host code `scratch` is only a stand-in for the symbol: its device address on the current
+// device comes from hipGetSymbolAddress (taken once per device, below) and only that address is
+// ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call per device.
+hipError_t scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 thread_local char g_last_error[512] = "";
 
@@ -112,10 +142,16 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t
                       "nvfp4_quantize launch");
 }
 
-nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s, float g_a,
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of nvfp4_gemm and nvfp4_gemm_noalloc. With noalloc the workspace arguments
+// are ignored: the partial sums go to the current device's scratch array.
+nvfp4_status gemm_entry(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s, float g_a,
                         const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, int64_t M,
                         int64_t N, int64_t K, const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
     if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return fail(NVFP4_ERR_SHAPE, "M or N too large");
@@ -175,10 +211,23 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     }
     if (expect != N) return fail(NVFP4_ERR_SEGMENTS, "segments cover [0, %lld), N = %lld", (long long)expect, (long long)N);
     const size_t need = nvfp4_gemm_workspace_bytes(M, N, K);
-    if (workspace_bytes < need || (need > 0 && !workspace))
-        return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
-    if (M == 0 || N == 0) return ok();
+    if (noalloc) {
+        if (need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES)
+            return fail(NVFP4_ERR_WORKSPACE,
+                        "nvfp4_gemm_noalloc: this shape needs %zu bytes of scratch, more than the fixed %zu bytes", need,
+                        (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        if (M == 0 || N == 0) return ok();
+        if (need > 0) {
+            const hipError_t e = scratch_of_current_device(&workspace);
+            if (e != hipSuccess) return hip_status(e, "nvfp4_gemm_noalloc: scratch address");
+        }
+    } else {
+        if (workspace_bytes < need || (need > 0 && !workspace))
+            return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+        if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+        if (M == 0 || N == 0) return ok();
+    }
     const hipStream_t st_ = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (M > nvfp4::SKINNY_MAX_M)
@@ -189,7 +238,27 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     else
         e = nvfp4::launch_gemm_skinny(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
                                       st_);
-    return hip_status(e, "nvfp4_gemm launch");
+    return hip_status(e, noalloc ? "nvfp4_gemm_noalloc launch" : "nvfp4_gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s, float g_a,
+                        const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, int64_t M,
+                        int64_t N, int64_t K, const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, M, N, K, segs, g_w, n_segs,
+                      workspace, workspace_bytes, false, stream);
+}
+
+nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                                float g_a, const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales,
+                                int64_t ldw_s, int64_t M, int64_t N, int64_t K, const nvfp4_segment* segs,
+                                const float* g_w, int32_t n_segs, void* stream) {
+    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, M, N, K, segs, g_w, n_segs,
+                      nullptr, 0, true, stream);
 }
 
 nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float* s_out,

@@ -262,3 +262,16 @@ def test_gdn_empty_and_token_by_token_need_no_workspace(L):
     assert gdn(L, B=0, ws=None, ws_bytes=0) == 0
     assert gdn(L, T=0, ws=None, ws_bytes=0) == 0
 
+
+def test_gemm_noalloc_rejects_before_any_launch(L):
+    """The allocation-free entry point validates like nvfp4_gemm and rejects shapes needing more than
+    its fixed per-GPU scratch (NVFP4_ERR_WORKSPACE) before touching the device."""
+    def call(M, N, K, lda_c, lda_s):
+        segs = seg_array([(0, N, 0, 0, A16, N, None, None)])
+        gw = (ctypes.c_float * 1)(1.0)
+        return L.nvfp4_gemm_noalloc(A16, lda_c, A16, lda_s, 1.0, A16, lda_c, A16, lda_s, M, N, K, segs, gw, 1, None)
+    assert L.nvfp4_gemm_workspace_bytes(64, 100000, 17408) > nv.NOALLOC_SCRATCH_BYTES
+    assert call(64, 100000, 17408, 8704, 1088) == 7
+    assert "scratch" in nv.last_error()
+    assert call(8, 64, 40, 32, 16) == 2
+    assert call(0, 64, 64, 32, 16) == 0
