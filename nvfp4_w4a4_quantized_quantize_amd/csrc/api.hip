@@ -235,6 +235,8 @@ nvfp4_status gemm_entry(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     else if (M > nvfp4::SKINNY_NARROW_M)
         e = nvfp4::launch_gemm_wide(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
                                     workspace, st_);
+    else if (nvfp4::gemv_supported(M, K))
+        e = nvfp4::launch_gemm_gemv(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp, st_);
     else
         e = nvfp4::launch_gemm_skinny(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
                                       st_);

@@ -32,6 +32,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t l
                            uint8_t* codes, int64_t ldc, uint8_t* scales, int64_t lds,
                            hipStream_t stream);
 
+// One activation row (K up to GEMV_MAX_K) runs on the weight-streaming GEMV kernel (with two rows
+// its VALU dot products cost more than the matrix-core path of the skinny kernel).
+constexpr int64_t GEMV_MAX_M = 1;
+constexpr int64_t GEMV_MAX_K = 32 * 64 * 16;
+bool gemv_supported(int64_t M, int64_t K);
+hipError_t launch_gemm_gemv(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                            const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                            int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+
 // Activation row counts up to SKINNY_NARROW_M run on the skinny (decode) kernel, up to SKINNY_MAX_M
 // on its wide variant (split K, partial sums in the workspace), larger ones on the tiled kernel.
 constexpr int64_t SKINNY_NARROW_M = 32;

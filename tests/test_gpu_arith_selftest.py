@@ -8,7 +8,7 @@ module libnvfp4_selftest.so runs the library's own helpers for these steps on th
 
 * quotient_fast against the IEEE division for every finite non-negative bf16 numerator and every
   binary32 significand of the divisor, in divisor binades spread over the whole fast range
-  (2^-100 .. 2^100); the IEEE division itself is pinned to numpy's binary32 division on the host;
+  (2^-80 .. 2^100); the IEEE division itself is pinned to numpy's binary32 division on the host;
 * the FP8 and FP4 conversions over every non-negative binary32 input (and +inf): monotone, in
   range, sign-symmetric, packing into the right nibbles;
 * the conversions at every grid point, every rounding midpoint and both binary32 neighbours of

@@ -1,6 +1,7 @@
 """GPU parity of the decode (M <= 64) GEMM path against the oracle.
 
-Activation row counts up to 32 run on the skinny kernel, 33 .. 64 on the wide (split-K) kernel:
+One activation row runs on the weight-streaming GEMV kernel (K up to 32768), up to 32 rows on the
+skinny kernel, 33 .. 64 on the wide (split-K) kernel:
 these tests cover every activation-tile count (M = 1 .. 64, ragged), both weight-tile widths of the
 skinny kernel (1 tile per wave for M <= 4, 2 above) at large N, K-splits over 1 .. 4 waves and over
 1 .. 8 workgroups with ragged chunk counts and a ragged final chunk, padded input strides, a reused
@@ -221,3 +222,17 @@ def test_decode_bf16_activation_pipeline(direction, M):
     assert (host(ac) == rac).all() and (host(as_) == ras).all()
     y, T = oracle.gemm_rows(rac, ras, g_a, rwc, rws, [0, case.N], np.array([g_w], np.float32), np.arange(M))
     check_bf16(out, y, T, case.name)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("K", [16, 1024 + 16, 32768, 32768 + 16])
+def test_gemv_rows_and_k_limits(M, K):
+    """One activation row runs on the weight-streaming kernel up to K = 32768 (a lane's share of
+    blocks ragged below that) and on the skinny kernel above, as do two rows; N not a multiple of the
+    4 rows of a workgroup."""
+    rng = np.random.default_rng(K * 3 + M)
+    N = 37
+    a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
+    out = run_single(a, w, 0.125, 2.5)
+    y, T = expect(a, w, 0.125, 2.5)
+    check_fp32(host(out), y, T, f"M={M} K={K}")
