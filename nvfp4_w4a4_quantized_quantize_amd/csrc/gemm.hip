@@ -29,12 +29,15 @@
 //    8-byte read. A sum does not depend on the order of its terms.
 //  * In a partial last column of tiles, a wave skips the 32-column fragments that lie wholly past N
 //    (no reads, dequantization or matrix instructions for them); its loads and barriers are the same.
+//    A tile of at most 128 columns stacks its 4 waves along M (64 rows each), so all of them work.
 //  * Tiles are ordered for the 8 XCDs (each with its own L2): workgroup b runs on XCD b % 8, so each
-//    XCD gets a contiguous range of tiles, walked in groups of 8 M-tiles so that concurrently
-//    running tiles share A and W panels in L2.
-//  * Epilogue: accumulators are staged per wave through LDS, 64 columns at a time; column ranges of
-//    a plain segment are scaled and written with 16-byte stores, 64 columns (whole 128-byte lines of
-//    bf16) or 32 at a time, other columns (gates, segment boundaries, the N tail) element by element.
+//    XCD gets a contiguous range of full-width tiles, walked in groups of 8 M-tiles so that
+//    concurrently running tiles share A and W panels in L2; the partial column's tiles run last.
+//  * Epilogue: the W fragment is the MFMA's first operand, so each lane holds runs of 4 consecutive
+//    output columns of one row. Accumulators are staged per wave through LDS (one 16-byte write per
+//    run), 64 columns at a time; column ranges of a plain segment are scaled and written with 16-byte
+//    stores, 64 columns (whole 128-byte lines of bf16) or 32 at a time, other columns (gates,
+//    segment boundaries, the N tail) element by element.
 #include "device_common.h"
 
 namespace nvfp4 {
@@ -112,15 +115,14 @@ __device__ __forceinline__ half2_t scale_pair(const u32x2& s, int c) {
                    : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[c >> 1], 1.0f, false);
 }
 
-// Codes of sub-chunk c (64 elements) for the 4 A and 4 W fragments of this lane.
-// (Only the first NB W fragments, and no A fragment when NB is 0.)
-template <int NB>
+// Codes of sub-chunk c (64 elements) for the first NA A and the first NB W fragments of this lane.
+template <int NA, int NB>
 __device__ __forceinline__ void read_codes(u32x4 (&ar)[4], u32x4 (&br)[4], const uint8_t* stage, const int (&a_row)[4],
                                            const int (&b_row)[4], int c, int lh) {
     const int q = 4 * lh + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (NB > 0)
+        if (i < NA)
             ar[i] = *reinterpret_cast<const u32x4*>(stage + A_CODES + a_row[i] * ROW_BYTES + ((q ^ swz(a_row[i])) << 4));
         if (i < NB)
             br[i] = *reinterpret_cast<const u32x4*>(stage + B_CODES + b_row[i] * ROW_BYTES + ((q ^ swz(b_row[i])) << 4));
@@ -130,12 +132,12 @@ __device__ __forceinline__ void read_codes(u32x4 (&ar)[4], u32x4 (&br)[4], const
 // This lane half's 8 scale bytes of each fragment row of a chunk (bytes 8 lh .. 8 lh + 7 of the row's
 // 16). When the chunk crosses K, bytes of blocks at or beyond K (nvalid of the row's 16 are valid)
 // are cleared, so that the code pieces read in their place contribute 0. (Fragments as in read_codes.)
-template <int NB>
+template <int NA, int NB>
 __device__ __forceinline__ void read_scales(u32x2 (&as)[4], u32x2 (&bs)[4], const uint8_t* stage, const int (&a_row)[4],
                                             const int (&b_row)[4], int lh, int nvalid) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (NB > 0) as[i] = *reinterpret_cast<const u32x2*>(stage + A_SCALES + a_row[i] * 16 + 8 * lh);
+        if (i < NA) as[i] = *reinterpret_cast<const u32x2*>(stage + A_SCALES + a_row[i] * 16 + 8 * lh);
         if (i < NB) bs[i] = *reinterpret_cast<const u32x2*>(stage + B_SCALES + b_row[i] * 16 + 8 * lh);
     }
     if (nvalid < 16) {  // only the chunk that crosses K; the asm keeps this a branch instead of selects
@@ -146,18 +148,22 @@ __device__ __forceinline__ void read_scales(u32x2 (&as)[4], u32x2 (&bs)[4], cons
             const uint32_t mask = nb >= 4 ? 0xffffffffu : (nb <= 0 ? 0u : (0xffffffffu >> (32 - 8 * nb)));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (NB > 0) as[i][d] &= mask;
+                if (i < NA) as[i][d] &= mask;
                 if (i < NB) bs[i][d] &= mask;
             }
         }
     }
 }
 
-// The main loop over the nk K chunks (see the kernel) for a wave whose first NJ of its 4 column
-// fragments hold columns below N: 4 in all but a partial last column of tiles, where it is 2 or 0 and
-// the fragments past N are neither read, dequantized nor multiplied. Every wave runs the same loads
-// and barriers.
-template <int NJ>
+// The main loop over the nk K chunks (see the kernel) for a wave with NA row fragments and NB column
+// fragments of 32: 4 x 4 in full tiles; in a partial last column of tiles the fragments past N are
+// neither read, dequantized nor multiplied (4 x 2, or 2 x 2 and 2 x 4 when the tile's waves are
+// stacked along M). Every wave runs the same loads and barriers.
+//
+// The W fragment is the MFMA's first operand, so the 32 x 32 result is the transposed output tile:
+// lane l holds output row lr = l % 32 of the fragment and, in register 4 g + e, output column
+// 8 g + 4 (l / 32) + e, i.e. four consecutive columns of one row per group g.
+template <int NA, int NB>
 __device__ __forceinline__ void main_loop(floatx16 (&acc)[4][4], uint8_t* smem, const Loader& ld, const int (&a_row)[4],
                                           const int (&b_row)[4], int lh, int64_t nk, int64_t K) {
     auto nvalid_of = [&](int64_t kc) -> int {
@@ -176,15 +182,15 @@ __device__ __forceinline__ void main_loop(floatx16 (&acc)[4][4], uint8_t* smem, 
     u32x4 araw[4], braw[4], anext[4], bnext[4];
     half2_t as2[4], bs2[4];
     half8_t aop[2][4], bop[2][4];
-    read_scales<NJ>(ascl, bscl, smem, a_row, b_row, lh, nvalid_of(0));
-    read_codes<NJ>(araw, braw, smem, a_row, b_row, 0, lh);
+    read_scales<NA, NB>(ascl, bscl, smem, a_row, b_row, lh, nvalid_of(0));
+    read_codes<NA, NB>(araw, braw, smem, a_row, b_row, 0, lh);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (NJ > 0) {
+        if (i < NA) {
             as2[i] = scale_pair(ascl[i], 0);
             aop[0][i] = dequant8(araw[i][0], as2[i][0]);
         }
-        if (i < NJ) {
+        if (i < NB) {
             bs2[i] = scale_pair(bscl[i], 0);
             bop[0][i] = dequant8(braw[i][0], bs2[i][0]);
         }
@@ -208,21 +214,21 @@ __device__ __forceinline__ void main_loop(floatx16 (&acc)[4][4], uint8_t* smem, 
             if (st == 12) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk kc + 1
                 __syncthreads();
-                read_scales<NJ>(ascl, bscl, nxt, a_row, b_row, lh, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
-                read_codes<NJ>(anext, bnext, nxt, a_row, b_row, 0, lh);
+                read_scales<NA, NB>(ascl, bscl, nxt, a_row, b_row, lh, nvalid_of(kc + 1 < nk ? kc + 1 : kc));
+                read_codes<NA, NB>(anext, bnext, nxt, a_row, b_row, 0, lh);
             } else if (j == 0) {
-                read_codes<NJ>(anext, bnext, cur, a_row, b_row, c + 1, lh);  // sub-chunk c + 1
+                read_codes<NA, NB>(anext, bnext, cur, a_row, b_row, c + 1, lh);  // sub-chunk c + 1
             }
             // operands of the next step (the next chunk's first step after step 15)
             const int s1 = (st + 1) & 15, c1 = s1 >> 2, j1 = s1 & 3;
             if (j1 == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (NJ > 0) {
+                    if (i < NA) {
                         araw[i] = anext[i];
                         as2[i] = scale_pair(ascl[i], c1);
                     }
-                    if (i < NJ) {
+                    if (i < NB) {
                         braw[i] = bnext[i];
                         bs2[i] = scale_pair(bscl[i], c1);
                     }
@@ -230,110 +236,42 @@ __device__ __forceinline__ void main_loop(floatx16 (&acc)[4][4], uint8_t* smem, 
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (NJ > 0) aop[nb][i] = dequant8(araw[i][j1], as2[i][j1 >> 1]);
-                if (i < NJ) bop[nb][i] = dequant8(braw[i][j1], bs2[i][j1 >> 1]);
+                if (i < NA) aop[nb][i] = dequant8(araw[i][j1], as2[i][j1 >> 1]);
+                if (i < NB) bop[nb][i] = dequant8(braw[i][j1], bs2[i][j1 >> 1]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NA; ++i)
 #pragma unroll
-                for (int jn = 0; jn < NJ; ++jn)
-                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[cb][i], bop[cb][jn], acc[i][jn], 0, 0, 0);
+                for (int jn = 0; jn < NB; ++jn)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop[cb][jn], aop[cb][i], acc[i][jn], 0, 0, 0);
             if (st >= 12) {
                 const uint32_t k2c = (uint32_t)((kc + 2 < nk ? kc + 2 : nk - 1) * BK);
                 ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12), k2c);
                 ld.piece(const_cast<uint8_t*>(cur), 2 * (st - 12) + 1, k2c);
             }
 #pragma unroll
-            for (int t = 0; t < 4 * NJ; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, NJ == 4 ? 4 : 6, 0);  // then the VALU
+            for (int t = 0; t < NA * NB; ++t) {
+                // one MFMA, then its share of the (NA + NB) dequantizations of 8 VALU instructions each
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8 * (NA + NB) / (NA * NB), 0);
             }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still target the LDS
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
-    const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
-    const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
-    int64_t M, int64_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, const SegParams sp) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 31;  // row of the MFMA fragment this lane feeds
-    const int lh = lane >> 5;  // lane half: which 8-element K group of an MFMA step
-
-    // ---- tile order: contiguous per XCD, grouped by GROUP_M M-tiles inside it -------------------
-    int tm, tn;
-    {
-        const int T = tiles_m * tiles_n;
-        const int bid = blockIdx.x;
-        const int xcd = bid & 7, local = bid >> 3;
-        const int q = T >> 3, rem = T & 7;
-        const int vt = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
-        const int per_group = GROUP_M * tiles_n;
-        const int g = vt / per_group, in_g = vt - g * per_group;
-        const int first_m = g * GROUP_M;
-        const int gm = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
-        tm = first_m + in_g % gm;
-        tn = in_g / gm;
-    }
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // per-lane LDS row indices of the MFMA fragments
-    int a_row[4], b_row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a_row[i] = wm * 128 + 32 * i + lr;
-        b_row[i] = wn * 128 + 32 * i + lr;
-    }
-
-    // ---- main loop --------------------------------------------------------------------------------
-    // Chunk kc lives in LDS stage kc % 2. One barrier per chunk, after step 11: every wave has then
-    // finished reading the current stage (its last code read feeds step 12) and has waited for its
-    // own loads of chunk kc + 1 (issued a whole chunk earlier), so after the barrier chunk kc + 1 is
-    // visible and the current stage is free for chunk kc + 2. Steps 12-15 then prefetch chunk
-    // kc + 1's scales and first codes, and step 15 dequantizes its first step, so the MFMA stream
-    // runs on across the chunk boundary.
-    const int64_t nk = (K + BK - 1) / BK;
-    if (nk > 0) {
-        const uint32_t rsub = lane >> 3;
-        const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, N, ldw_c),
-                        tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, N, ldw_s),
-                        (uint32_t)lda_c, (uint32_t)ldw_c, (uint32_t)lda_s, (uint32_t)ldw_s,
-                        rsub * (uint32_t)lda_c, rsub * (uint32_t)ldw_c, (uint32_t)lane * (uint32_t)lda_s,
-                        (uint32_t)lane * (uint32_t)ldw_s, 16u * ((lane & 7) ^ rsub), wave};
-        const int64_t wcol0 = n0 + wn * 128;  // first column of this wave's fragments
-        if (wcol0 + 64 < N)
-            main_loop<4>(acc, smem, ld, a_row, b_row, lh, nk, K);
-        else if (wcol0 < N)
-            main_loop<2>(acc, smem, ld, a_row, b_row, lh, nk, K);
-        else
-            main_loop<0>(acc, smem, ld, a_row, b_row, lh, nk, K);
-    }
-    __syncthreads();  // all waves done with the LDS stages before the epilogue reuses them
-
-    // ---- epilogue ---------------------------------------------------------------------------------
-    // Each wave stages two of its 128 x 32 column groups (64 columns) of FP32 accumulators at a time
-    // in a private LDS region (68-float row pitch). A 64-column pair inside one plain segment is then
-    // scaled and written with 16-byte stores, lane -> row lane / 8 (+8 per pass), columns
-    // (lane % 8) * 8 .. + 8, so that every row of the pair is written in whole 128-byte lines; other
-    // 32-column groups of a plain segment use the same stores with 4 lanes per row, and gate
-    // segments, segment boundaries and the N tail go element by element, lane -> column lane % 32.
-    float* ep = reinterpret_cast<float*>(smem) + wave * (128 * EP_PITCH);
-    const int64_t row_base = m0 + wm * 128;
-    const int nrows = (int)(M - row_base < 128 ? (M - row_base > 0 ? M - row_base : 0) : 128);
+// Writes one wave's outputs. acc[i][jn][4 g + e] is output (row0 + 32 i + lr, col0 + 32 jn + 8 g + 4 lh + e)
+// (i < NA, jn < NB). Each pair of column fragments (64 columns) is staged in the wave's LDS region ep
+// (32 NA rows, EP_PITCH floats apart) with one 16-byte write per group; then a pair inside one plain
+// segment is scaled and written with 16-byte stores, 8 lanes per row (whole 128-byte lines of bf16),
+// other 32-column fragments of a plain segment with 4 lanes per row, and gate segments, segment
+// boundaries and the N tail element by element, lane -> column lr, rows of parity lh.
+template <int NA, int NB>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const SegParams& sp, int64_t row0, int64_t col0,
+                                           int64_t M, int64_t N, int lane, float* ep) {
+    constexpr int RW = 32 * NA;  // rows of the wave
+    const int lr = lane & 31, lh = lane >> 5;
+    const int nrows = (int)(M - row0 < RW ? (M - row0 > 0 ? M - row0 : 0) : RW);
     auto plain_run = [&](int64_t c0, int width) -> int {  // segment of [c0, c0 + width) if written by vector stores, else -1
         const int s0 = segment_of(sp, c0);
         const bool ok = c0 + width <= N && c0 + width - 1 < sp.n_end[s0] && sp.epilogue[s0] == NVFP4_EPI_NONE &&
@@ -354,51 +292,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         }
     };
 #pragma unroll
-    for (int jp = 0; jp < 2; ++jp) {
+    for (int jp = 0; jp < NB / 2; ++jp) {
+        const int64_t c0 = col0 + 64 * jp;  // first column of this 64-column pair
+        if (c0 >= N) break;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NA; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    ep[(32 * i + (r >> 2) * 8 + lh * 4 + (r & 3)) * EP_PITCH + 32 * h + lr] = acc[i][2 * jp + h][r];
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(ep + (32 * i + lr) * EP_PITCH + 32 * h + 8 * g + 4 * lh) =
+                        f32x4{acc[i][2 * jp + h][4 * g], acc[i][2 * jp + h][4 * g + 1], acc[i][2 * jp + h][4 * g + 2],
+                              acc[i][2 * jp + h][4 * g + 3]};
         // the region is private to this wave: its own LDS writes completing is enough
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int64_t c0 = n0 + wn * 128 + 64 * jp;  // first column of this 64-column pair
-        if (c0 < N) {
-            const int s64 = plain_run(c0, 64);
-            if (s64 >= 0) {
-                const float scale = sp.scale[s64];
-                const int64_t ldo = sp.ldo[s64];
-                const bool bf16 = sp.out_dtype[s64] == NVFP4_OUT_BF16;
-                uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s64]);
-                const int64_t j0 = c0 - sp.n_begin[s64] + (lane & 7) * 8;
-                if (nrows == 128 && bf16) {  // full rows, bf16: no per-row masks, no per-store type test
-                    uint8_t* dst = outp + ((row_base + (lane >> 3)) * ldo + j0) * 2;
-                    const int64_t step8 = 8 * ldo * 2;  // bytes between a lane's consecutive rows
+        const int s64 = plain_run(c0, 64);
+        if (s64 >= 0) {
+            const float scale = sp.scale[s64];
+            const int64_t ldo = sp.ldo[s64];
+            const bool bf16 = sp.out_dtype[s64] == NVFP4_OUT_BF16;
+            uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s64]);
+            const int64_t j0 = c0 - sp.n_begin[s64] + (lane & 7) * 8;
+            if (nrows == RW && bf16) {  // full rows, bf16: no per-row masks, no per-store type test
+                uint8_t* dst = outp + ((row0 + (lane >> 3)) * ldo + j0) * 2;
+                const int64_t step8 = 8 * ldo * 2;  // bytes between a lane's consecutive rows
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        f32x4 v[16];
-#pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const float* src = ep + ((lane >> 3) + 8 * (8 * half + p)) * EP_PITCH + (lane & 7) * 8;
-                            v[2 * p] = *reinterpret_cast<const f32x4*>(src);
-                            v[2 * p + 1] = *reinterpret_cast<const f32x4*>(src + 4);
-                        }
-#pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const f32x4 y0 = v[2 * p] * scale, y1 = v[2 * p + 1] * scale;
-                            u32x4 packed;
-                            packed[0] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[0], (__bf16)y0[1]});
-                            packed[1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[2], (__bf16)y0[3]});
-                            packed[2] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[0], (__bf16)y1[1]});
-                            packed[3] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[2], (__bf16)y1[3]});
-                            *reinterpret_cast<u32x4*>(dst + (8 * half + p) * step8) = packed;
-                        }
-                    }
-                } else
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
+                for (int half = 0; half < RW / 64; ++half) {
                     f32x4 v[16];
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
@@ -408,59 +327,168 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     }
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
-                        const int rr = (lane >> 3) + 8 * (8 * half + p);
-                        if (rr < nrows) store8(outp, bf16, (row_base + rr) * ldo + j0, v[2 * p] * scale, v[2 * p + 1] * scale);
+                        const f32x4 y0 = v[2 * p] * scale, y1 = v[2 * p + 1] * scale;
+                        u32x4 packed;
+                        packed[0] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[0], (__bf16)y0[1]});
+                        packed[1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0[2], (__bf16)y0[3]});
+                        packed[2] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[0], (__bf16)y1[1]});
+                        packed[3] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y1[2], (__bf16)y1[3]});
+                        *reinterpret_cast<u32x4*>(dst + (8 * half + p) * step8) = packed;
                     }
                 }
-            } else {
+            } else
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int64_t c1 = c0 + 32 * h;  // first column of this 32-column group
-                    if (c1 >= N) break;
-                    const int s32 = plain_run(c1, 32);
-                    if (s32 >= 0) {
-                        const float scale = sp.scale[s32];
-                        const int64_t ldo = sp.ldo[s32];
-                        const bool bf16 = sp.out_dtype[s32] == NVFP4_OUT_BF16;
-                        uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s32]);
-                        const int64_t j0 = c1 - sp.n_begin[s32] + (lane & 3) * 8;
+            for (int half = 0; half < RW / 64; ++half) {
+                f32x4 v[16];
 #pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const int rr = (lane >> 2) + 16 * p;
-                            const float* src = ep + rr * EP_PITCH + 32 * h + (lane & 3) * 8;
-                            const f32x4 y0 = *reinterpret_cast<const f32x4*>(src), y1 = *reinterpret_cast<const f32x4*>(src + 4);
-                            if (rr < nrows) store8(outp, bf16, (row_base + rr) * ldo + j0, y0 * scale, y1 * scale);
-                        }
-                    } else {
-                        const int64_t col = c1 + lr;
-                        if (col < N) {
-                            const int s = segment_of(sp, col);
-                            const float scale = sp.scale[s];
-                            const int epi = sp.epilogue[s];
-                            const int64_t j = col - sp.n_begin[s];
-                            const int64_t ldo = sp.ldo[s];
-                            const bool f32out = sp.out_dtype[s] == NVFP4_OUT_F32;
-                            uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s]);
-                            float a_coef = 0.0f, dtb = 0.0f;
-                            if (epi == NVFP4_EPI_GDN_DECAY) {
-                                a_coef = expf(sp.A_log[s][j]);
-                                dtb = sp.dt_bias[s][j];
-                            }
-                            for (int rr = lh; rr < nrows; rr += 2) {
-                                const float y = apply_gate(ep[rr * EP_PITCH + 32 * h + lr] * scale, epi, a_coef, dtb);
-                                const int64_t off = (row_base + rr) * ldo + j;
-                                if (f32out)
-                                    reinterpret_cast<float*>(outp)[off] = y;
-                                else
-                                    reinterpret_cast<__bf16*>(outp)[off] = (__bf16)y;
-                            }
-                        }
+                for (int p = 0; p < 8; ++p) {
+                    const float* src = ep + ((lane >> 3) + 8 * (8 * half + p)) * EP_PITCH + (lane & 7) * 8;
+                    v[2 * p] = *reinterpret_cast<const f32x4*>(src);
+                    v[2 * p + 1] = *reinterpret_cast<const f32x4*>(src + 4);
+                }
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int rr = (lane >> 3) + 8 * (8 * half + p);
+                    if (rr < nrows) store8(outp, bf16, (row0 + rr) * ldo + j0, v[2 * p] * scale, v[2 * p + 1] * scale);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t c1 = c0 + 32 * h;  // first column of this 32-column fragment
+                if (c1 >= N) break;
+                const int s32 = plain_run(c1, 32);
+                if (s32 >= 0) {
+                    const float scale = sp.scale[s32];
+                    const int64_t ldo = sp.ldo[s32];
+                    const bool bf16 = sp.out_dtype[s32] == NVFP4_OUT_BF16;
+                    uint8_t* outp = reinterpret_cast<uint8_t*>(sp.out[s32]);
+                    const int64_t j0 = c1 - sp.n_begin[s32] + (lane & 3) * 8;
+#pragma unroll
+                    for (int p = 0; p < RW / 16; ++p) {
+                        const int rr = (lane >> 2) + 16 * p;
+                        const float* src = ep + rr * EP_PITCH + 32 * h + (lane & 3) * 8;
+                        const f32x4 y0 = *reinterpret_cast<const f32x4*>(src), y1 = *reinterpret_cast<const f32x4*>(src + 4);
+                        if (rr < nrows) store8(outp, bf16, (row0 + rr) * ldo + j0, y0 * scale, y1 * scale);
+                    }
+                } else {
+                    const int64_t col = c1 + lr;
+                    if (col < N) {
+                        const ColumnOut c = column_out(sp, col);
+                        for (int rr = lh; rr < nrows; rr += 2) column_store(c, row0 + rr, ep[rr * EP_PITCH + 32 * h + lr]);
                     }
                 }
             }
         }
         // the next pair's staging writes must not pass this pair's reads
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
+    const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
+    const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
+    int64_t M, int64_t N, int64_t K, int32_t tiles_m, const SegParams sp) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31;  // row of the MFMA fragment this lane feeds
+    const int lh = lane >> 5;  // lane half: which 8-element K group of an MFMA step
+
+    // ---- tile order ---------------------------------------------------------------------------------
+    // Tiles of the full-width tile columns come first: contiguous per XCD, grouped by GROUP_M M-tiles
+    // inside it. The tiles of a partial last column (fewer than BN columns of N) come last, one per
+    // M-tile, so that the cheaper ones fill the final, partly occupied round of workgroups.
+    int tm, tn;
+    {
+        const int tn_full = (int)(N / BN);
+        const int T = tiles_m * tn_full;
+        const int bid = blockIdx.x;
+        if (bid >= T) {
+            tm = bid - T;
+            tn = tn_full;
+        } else {
+            const int xcd = bid & 7, local = bid >> 3;
+            const int q = T >> 3, rem = T & 7;
+            const int vt = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
+            const int per_group = GROUP_M * tn_full;
+            const int g = vt / per_group, in_g = vt - g * per_group;
+            const int first_m = g * GROUP_M;
+            const int gm = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
+            tm = first_m + in_g % gm;
+            tn = in_g / gm;
+        }
+    }
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    // Wave layout: 2 x 2 waves of 128 x 128 in a tile with more than 128 columns; with at most 128
+    // columns, 4 x 1 waves of 64 rows x 128 columns (so that all four waves have work).
+    const int64_t n_tile = N - n0 < BN ? N - n0 : BN;
+    const bool stacked = n_tile <= 128;
+    const int wm = stacked ? wave : wave >> 1, wn = stacked ? 0 : wave & 1;
+    const int64_t row0 = m0 + (stacked ? 64 : 128) * wm;  // first output row of this wave
+    const int64_t col0 = n0 + 128 * wn;                    // first output column of this wave
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // per-lane LDS row indices of the MFMA fragments (stacked: only the first two A fragments are used)
+    int a_row[4], b_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a_row[i] = (int)(row0 - m0) + 32 * (stacked ? (i & 1) : i) + lr;
+        b_row[i] = (int)(col0 - n0) + 32 * i + lr;
+    }
+
+    // ---- main loop --------------------------------------------------------------------------------
+    // Chunk kc lives in LDS stage kc % 2. One barrier per chunk, after step 11: every wave has then
+    // finished reading the current stage (its last code read feeds step 12) and has waited for its
+    // own loads of chunk kc + 1 (issued a whole chunk earlier), so after the barrier chunk kc + 1 is
+    // visible and the current stage is free for chunk kc + 2. Steps 12-15 then prefetch chunk
+    // kc + 1's scales and first codes, and step 15 dequantizes its first step, so the MFMA stream
+    // runs on across the chunk boundary.
+    const int64_t nk = (K + BK - 1) / BK;
+    const int64_t n_wave = N - col0;  // columns of this wave that exist (> 0 in either layout)
+    const uint32_t rsub = lane >> 3;
+    const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, N, ldw_c),
+                    tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, N, ldw_s),
+                    (uint32_t)lda_c, (uint32_t)ldw_c, (uint32_t)lda_s, (uint32_t)ldw_s,
+                    rsub * (uint32_t)lda_c, rsub * (uint32_t)ldw_c, (uint32_t)lane * (uint32_t)lda_s,
+                    (uint32_t)lane * (uint32_t)ldw_s, 16u * ((lane & 7) ^ rsub), wave};
+    if (nk > 0) {
+        if (stacked) {
+            if (n_wave <= 64)
+                main_loop<2, 2>(acc, smem, ld, a_row, b_row, lh, nk, K);
+            else
+                main_loop<2, 4>(acc, smem, ld, a_row, b_row, lh, nk, K);
+        } else {
+            if (n_wave <= 64)
+                main_loop<4, 2>(acc, smem, ld, a_row, b_row, lh, nk, K);
+            else
+                main_loop<4, 4>(acc, smem, ld, a_row, b_row, lh, nk, K);
+        }
+    }
+
+    // ---- epilogue -----------------------------------------------------------------------------------
+    __syncthreads();  // all waves done with the LDS stages before the epilogue reuses them
+    float* ep = reinterpret_cast<float*>(smem) + wave * (128 * EP_PITCH);
+    if (stacked) {
+        if (n_wave <= 64)
+            store_tile<2, 2>(acc, sp, row0, col0, M, N, lane, ep);
+        else
+            store_tile<2, 4>(acc, sp, row0, col0, M, N, lane, ep);
+    } else {
+        if (n_wave <= 64)
+            store_tile<4, 2>(acc, sp, row0, col0, M, N, lane, ep);
+        else
+            store_tile<4, 4>(acc, sp, row0, col0, M, N, lane, ep);
     }
 }
 
@@ -472,8 +500,7 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(tiles_m * tiles_n)), dim3(NTHREADS), 0, stream, a_codes,
-                       lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, (int32_t)tiles_m,
-                       (int32_t)tiles_n, sp);
+                       lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, (int32_t)tiles_m, sp);
     return hipGetLastError();
 }
 

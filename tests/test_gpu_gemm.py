@@ -92,6 +92,57 @@ def test_multi_segment_ragged_boundaries_and_gates():
             check_bf16(out, ys, Ts, f"segment {s}")
 
 
+# Partial last tile columns of every width class, with and without gate columns in them: the prefill
+# kernel stacks its waves along M when a tile has at most 128 columns (64 or 128 of them per wave) and
+# keeps 2 x 2 waves otherwise (the second column pair with 32 or 64 columns); tiles whose fragments all
+# lie in plain vector-aligned segments are written straight from the registers, the others (gates,
+# unaligned boundaries, a ragged N tail) element by element in a second launch.
+_LAYOUTS = {
+    "gates_in_64_col_tail": [(256, 1.5, "none", torch.bfloat16), (32, 0.7, "sigmoid", torch.float32),
+                             (32, 0.9, "gdn_decay", torch.float32)],
+    "gates_in_104_col_tail": [(512, 1.5, "none", torch.bfloat16), (40, 2.0, "none", torch.float32),
+                              (32, 0.7, "sigmoid", torch.float32), (32, 0.9, "gdn_decay", torch.float32)],
+    "direct_96_col_tail": [(352, 1.25, "none", torch.bfloat16)],
+    "direct_192_col_tail": [(448, 0.5, "none", torch.float32)],
+    "direct_160_col_tail": [(160, 0.75, "none", torch.bfloat16), (256, 3.0, "none", torch.float32)],
+    "ragged_72_col_tail": [(256, 1.0, "none", torch.bfloat16), (72, 2.5, "none", torch.bfloat16)],
+    "gates_mid_n": [(256, 1.0, "none", torch.bfloat16), (64, 0.6, "sigmoid", torch.float32),
+                    (256, 1.1, "none", torch.bfloat16), (64, 0.8, "gdn_decay", torch.float32),
+                    (256, 1.2, "none", torch.float32)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(_LAYOUTS))
+def test_tile_layouts_and_epilogue_kernels(name):
+    rng = np.random.default_rng(sum(map(ord, name)))
+    M, K = 300, 528  # a ragged second M tile and a K tail of one block
+    layout = _LAYOUTS[name]
+    N = sum(n for n, *_ in layout)
+    a, w = random_nvfp4(rng, M, K, 0x20, 0x50), random_nvfp4(rng, N, K, 0x20, 0x50)
+    spec = []
+    for n, gw, epi, dt in layout:
+        al = db = None
+        if epi == "gdn_decay":
+            al = (rng.standard_normal(n) * 0.5).astype(np.float32)
+            db = (rng.standard_normal(n) * 0.5).astype(np.float32)
+        spec.append((n, gw, epi, dt, al, db))
+    g_a = np.float32(2.0 ** -6)
+    outs = run_gemm(a, w, g_a, spec, K)
+    (y, T), bounds = oracle_y(a, w, g_a, spec, np.arange(M))
+    for s, out in enumerate(outs):
+        lo, hi = bounds[s], bounds[s + 1]
+        ys, Ts = y[:, lo:hi], T[:, lo:hi]
+        n, _, epi, dt, al, db = spec[s]
+        if epi == "sigmoid":
+            check_sigmoid(host(out), ys, Ts, oracle.sigmoid(ys))
+        elif epi == "gdn_decay":
+            check_decay(host(out), ys, Ts, oracle.gdn_decay(ys, al, db), al, db)
+        elif dt == torch.float32:
+            check_fp32(host(out), ys, Ts, f"{name} segment {s}")
+        else:
+            check_bf16(out, ys, Ts, f"{name} segment {s}")
+
+
 def test_fused_equals_unfused_bitwise_and_repeatable():
     rng = np.random.default_rng(7)
     M, K = 200, 640
