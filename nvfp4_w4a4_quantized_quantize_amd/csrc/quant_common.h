@@ -12,6 +12,14 @@ typedef uint32_t qu32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float qf32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 qbf16x2 __attribute__((ext_vector_type(2)));
+
+// Both values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32, packed lo | hi << 16.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(qf32x2{lo, hi}, qbf16x2));
+}
+
 // E4M3FN round-to-nearest-even with saturation at 448, for a non-negative input. The gfx950
 // conversion rounds to nearest even in the OCP E4M3FN format but turns inputs of 464 and above into
 // NaN, so clamp first.
@@ -67,7 +75,8 @@ __device__ __forceinline__ Block16 encode_block16(const float (&f)[16], float g)
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
 
     const float t = 6.0f * g;
-    const float s_raw = __fdiv_rn(amax, t);
+    // RN32(amax / t): amax is the magnitude of a bf16 value, so quotient_fast applies inside its range
+    const float s_raw = quotient_fast_ok(t, amax) ? quotient_fast(amax, t, __builtin_amdgcn_rcpf(t)) : __fdiv_rn(amax, t);
     const uint32_t sb = e4m3_rne_sat(s_raw);
     const float s = e4m3_to_f32(sb);
     const float S = s * g;

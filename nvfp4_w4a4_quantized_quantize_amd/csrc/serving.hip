@@ -116,19 +116,18 @@ __device__ __forceinline__ double sum_squares16(const qu32x4& p0, const qu32x4& 
     return ss;
 }
 
-__device__ __forceinline__ void norm_encode_block(const qu32x4& p0, const qu32x4& p1, const qu32x4& w0,
-                                                  const qu32x4& w1, int64_t b, float r, float g,
-                                                  uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
-                                                  uint16_t* __restrict__ y_row) {
+// wf: the block's 16 norm weights as FP32 (exact bf16 values).
+__device__ __forceinline__ void norm_encode_block(const qu32x4& p0, const qu32x4& p1, const float* wf, int64_t b,
+                                                  float r, float g, uint8_t* __restrict__ codes_row,
+                                                  uint8_t* __restrict__ scales_row, uint16_t* __restrict__ y_row) {
     const uint32_t xv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-    const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
     float f[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float y1lo = (float)(__bf16)(bf16_lo(xv[i]) * r);
-        const float y1hi = (float)(__bf16)(bf16_hi(xv[i]) * r);
-        f[2 * i] = (float)(__bf16)(y1lo * bf16_lo(wv[i]));
-        f[2 * i + 1] = (float)(__bf16)(y1hi * bf16_hi(wv[i]));
+    for (int i = 0; i < 8; ++i) {  // two elements per bf16 rounding instruction
+        const uint32_t y1 = bf16x2_rne(bf16_lo(xv[i]) * r, bf16_hi(xv[i]) * r);
+        const uint32_t y = bf16x2_rne(bf16_lo(y1) * wf[2 * i], bf16_hi(y1) * wf[2 * i + 1]);
+        f[2 * i] = bf16_lo(y);
+        f[2 * i + 1] = bf16_hi(y);
     }
     const Block16 q = encode_block16(f, g);
     __builtin_nontemporal_store(qu32x2{q.c0, q.c1}, reinterpret_cast<qu32x2*>(codes_row + 8 * b));
@@ -168,8 +167,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
     uint16_t* y_row = y_out ? y_out + row * ldy : nullptr;
 
     if constexpr (NBL > 0) {
-        // the row is loaded first; the norm weights are staged once per workgroup in LDS meanwhile
-        __shared__ __attribute__((aligned(16))) uint16_t w_lds[NBL * 64 * 16];
+        // the row is loaded first; the norm weights are staged once per workgroup in LDS meanwhile,
+        // widened to FP32 (exact)
+        __shared__ __attribute__((aligned(16))) float w_lds[NBL * 64 * 16];
         qu32x4 p[NBL][2];
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
@@ -180,8 +180,19 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
                 p[j][1] = __builtin_nontemporal_load(src + 1);
             }
         }
-        for (int64_t i = threadIdx.x; i < nb * 2; i += 256)
-            reinterpret_cast<qu32x4*>(w_lds)[i] = reinterpret_cast<const qu32x4*>(w)[i];
+        for (int64_t i = threadIdx.x; i < nb * 2; i += 256) {
+            const qu32x4 wq = reinterpret_cast<const qu32x4*>(w)[i];  // 8 weights
+            qu32x4 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                lo[2 * e] = wq[e] << 16;
+                lo[2 * e + 1] = wq[e] & 0xffff0000u;
+                hi[2 * e] = wq[2 + e] << 16;
+                hi[2 * e + 1] = wq[2 + e] & 0xffff0000u;
+            }
+            reinterpret_cast<qu32x4*>(w_lds)[2 * i] = lo;
+            reinterpret_cast<qu32x4*>(w_lds)[2 * i + 1] = hi;
+        }
         __syncthreads();
         if (row >= rows) return;
         double ss = 0.0;
@@ -192,10 +203,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int64_t b = lane + 64 * j;
-            if (b < nb) {
-                const qu32x4* wl = reinterpret_cast<const qu32x4*>(w_lds + 16 * b);
-                norm_encode_block(p[j][0], p[j][1], wl[0], wl[1], b, r, g, codes_row, scales_row, y_row);
-            }
+            if (b < nb) norm_encode_block(p[j][0], p[j][1], w_lds + 16 * b, b, r, g, codes_row, scales_row, y_row);
         }
     } else {
         double ss = 0.0;
@@ -207,7 +215,16 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
         for (int64_t b = lane; b < nb; b += 64) {
             const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
             const qu32x4* wsrc = reinterpret_cast<const qu32x4*>(w + 16 * b);
-            norm_encode_block(src[0], src[1], wsrc[0], wsrc[1], b, r, g, codes_row, scales_row, y_row);
+            const qu32x4 w0 = wsrc[0], w1 = wsrc[1];
+            float wf[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wf[2 * i] = bf16_lo(w0[i]);
+                wf[2 * i + 1] = bf16_hi(w0[i]);
+                wf[8 + 2 * i] = bf16_lo(w1[i]);
+                wf[8 + 2 * i + 1] = bf16_hi(w1[i]);
+            }
+            norm_encode_block(src[0], src[1], wf, b, r, g, codes_row, scales_row, y_row);
         }
     }
 }
