@@ -65,7 +65,8 @@ def _eval(st, v, S=None):
 
 def _with_neighbours(points):
     p = np.asarray(points, dtype=np.float32)
-    return np.unique(np.concatenate([p, np.nextafter(p, np.float32(-np.inf)), np.nextafter(p, np.float32(np.inf))]))
+    with np.errstate(over="ignore"):  # the largest float's upper neighbour is +inf, kept on purpose
+        return np.unique(np.concatenate([p, np.nextafter(p, np.float32(-np.inf)), np.nextafter(p, np.float32(np.inf))]))
 
 
 def e4m3_points():
