@@ -268,6 +268,22 @@ def test_k_zero_writes_zero_and_empty_shapes(M):
     assert out.shape == (0, N)
 
 
+@pytest.mark.parametrize("M", [5, 40, 300])
+def test_k_zero_gates_see_zero(M):
+    """K = 0 with gate segments, on each kernel: the gates of y = 0 (sigmoid 1/2, decay of dt_bias)."""
+    rng = np.random.default_rng(M)
+    a_log = (rng.standard_normal(32) * 0.5).astype(np.float32)
+    dt_b = (rng.standard_normal(32) * 0.5).astype(np.float32)
+    a = torch.empty((M, 0), dtype=torch.uint8, device=DEV)
+    w = torch.empty((64, 0), dtype=torch.uint8, device=DEV)
+    sig, dec = nv.gemm(a, a, 1.0, w, w, [nv.Segment(32, 1.0, "sigmoid"),
+                                         nv.Segment(32, 1.0, "gdn_decay", torch.float32,
+                                                    torch.from_numpy(a_log).to(DEV), torch.from_numpy(dt_b).to(DEV))])
+    y = np.zeros((M, 32))
+    check_sigmoid(host(sig), y, y, oracle.sigmoid(y))
+    check_decay(host(dec), y, y, oracle.gdn_decay(y, a_log, dt_b), a_log, dt_b)
+
+
 def test_tiny_workload_end_to_end():
     """Tiny config: both operands quantized on the GPU from bf16, single segment, FP32 out."""
     case = wl.C1
