@@ -14,11 +14,11 @@
 //    every output bit, does not depend on N, the column tile or the segment table (a fused GEMM and
 //    the same modules called one by one agree bitwise).
 //  * Operands go straight from global memory into registers: each weight byte is used by exactly
-//    one wave, so staging through LDS would buy nothing. Lane (r, g), r = lane % 16 and
-//    g = lane / 16, loads the 32 code bytes (64 elements) at byte 32g of row r's 128-byte chunk and
-//    the 4 scale bytes of those elements. Activation rows are loaded the same way, so lane group g
-//    holds the same K elements of both operands, as the matrix instruction requires; within a chunk
-//    the 256 elements are thus summed in a permuted order, which a sum does not depend on.
+//    one wave. Four consecutive lanes read one contiguous run of a row (see RowFrag), and
+//    ds_bpermute then moves the data into the matrix instruction's layout. Activation rows are loaded
+//    and moved the same way, so lane group g holds the same K elements of both operands, as the
+//    matrix instruction requires; within a chunk the 256 elements are thus summed in a permuted
+//    order, which a sum does not depend on.
 //  * v_mfma_f32_16x16x32_f16 with 16 weight rows as the rows of A and 16 activation rows as the
 //    columns of B; at step j (0..7) each lane feeds its elements [8j, 8j + 8). Both operands are
 //    dequantized to FP16 exactly (see dequant8), products are exact in FP32 and accumulate in FP32.
@@ -38,44 +38,82 @@ constexpr int CHUNK = 256;  // K elements per chunk: 128 code bytes and 16 scale
 constexpr int DEPTH = 2;    // chunks in flight ahead of the one being multiplied
 
 // One lane's share of one row of a chunk: 64 codes (two 16-byte pieces) and their 4 scale bytes.
+//
+// Loads: lane l reads row l / 4 of a 16-row tile, bytes 64h + 16q (q = l % 4, h = 0, 1) of the
+// chunk's 128 code bytes and bytes 4q .. 4q + 3 of its 16 scale bytes, so that each group of four
+// consecutive lanes reads one contiguous run: a load whose lanes each hit another row costs the
+// memory pipeline several times as much per byte (measured with loads alone: the decode kernels' loads
+// took 19.7 us laid out that way, 13.6 us with four-lane runs, for the 17408 x 5120 weights and 16
+// activation rows). The matrix instruction wants lane r + 16g to hold row r; to_operand moves the data there
+// with ds_bpermute, after which lane (r, g) holds elements [128h + 32g, 128h + 32g + 32) of the chunk
+// (h = 0, 1) in c[h] and the scale bytes of its four blocks, in order, in s. Both operands are moved
+// the same way, so lane group g holds the same K elements of both, as the matrix instruction needs;
+// within a chunk the 256 elements are thus summed in a permuted order.
 struct RowFrag {
     u32x4 c[2];
     uint32_t s;
 };
 
-// codes/scales point at the lane's first byte of the row (row base + 32g, row base + 4g).
+// codes/scales point at the lane's first byte of the row (row base + 16q, row base + 4q).
 __device__ __forceinline__ void load_full(const uint8_t* codes, const uint8_t* scales, int64_t c, RowFrag& f) {
     const uint8_t* p = codes + c * (CHUNK / 2);
     f.c[0] = *reinterpret_cast<const u32x4*>(p);
-    f.c[1] = *reinterpret_cast<const u32x4*>(p + 16);
+    f.c[1] = *reinterpret_cast<const u32x4*>(p + 64);
     f.s = *reinterpret_cast<const uint32_t*>(scales + c * (CHUNK / 16));
 }
 
 // The chunk that crosses K: only bytes of elements below K are read; the rest is zero, and a zero
 // scale byte makes a block contribute 0. K is a multiple of 16, so a piece is full, half or empty.
-__device__ __forceinline__ void load_tail(const uint8_t* codes, const uint8_t* scales, int64_t c, int g, int64_t K,
+__device__ __forceinline__ void load_tail(const uint8_t* codes, const uint8_t* scales, int64_t c, int q, int64_t K,
                                           RowFrag& f) {
-    const int64_t cvalid = K / 2 - (c * (CHUNK / 2) + 32 * g);
-    const int64_t svalid = K / 16 - (c * (CHUNK / 16) + 4 * g);
     const uint8_t* p = codes + c * (CHUNK / 2);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int64_t v = cvalid - 16 * h;
+        const int64_t v = K / 2 - (c * (CHUNK / 2) + 64 * h + 16 * q);
         if (v >= 16) {
-            f.c[h] = *reinterpret_cast<const u32x4*>(p + 16 * h);
+            f.c[h] = *reinterpret_cast<const u32x4*>(p + 64 * h);
         } else if (v >= 8) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(p + 16 * h);
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(p + 64 * h);
             f.c[h] = u32x4{lo[0], lo[1], 0u, 0u};
         } else {
             f.c[h] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    const uint8_t* q = scales + c * (CHUNK / 16);
-    uint32_t s = 0;
+    const int64_t svalid = K / 16 - (c * (CHUNK / 16) + 4 * q);
+    const uint8_t* sp = scales + c * (CHUNK / 16);
+    uint32_t sv = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (i < svalid) s |= (uint32_t)q[i] << (8 * i);
-    f.s = s;
+        if (i < svalid) sv |= (uint32_t)sp[i] << (8 * i);
+    f.s = sv;
+}
+
+// Source lanes of this lane's operand data (byte addresses for ds_bpermute) and the byte selector
+// that keeps its two scale pairs.
+struct OperandLanes {
+    int codes, scales0, scales1;
+    uint32_t sel;
+};
+
+__device__ __forceinline__ OperandLanes operand_lanes(int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    // codes: lane 4r + g loaded row r's bytes 64h + 16g; scales: bytes 2g, 2g + 1 of the row's 16
+    // (blocks of h = 0) sit in lane 4r + g / 2, bytes 8 + 2g, 9 + 2g (h = 1) in lane 4r + 2 + g / 2
+    return {4 * (4 * r + g), 4 * (4 * r + (g >> 1)), 4 * (4 * r + 2 + (g >> 1)), (g & 1) ? 0x07060302u : 0x05040100u};
+}
+
+__device__ __forceinline__ uint32_t lane_read(int src, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v);
+}
+
+__device__ __forceinline__ RowFrag to_operand(const RowFrag& f, const OperandLanes& L) {
+    RowFrag o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.c[h][e] = lane_read(L.codes, f.c[h][e]);
+    o.s = __builtin_amdgcn_perm(lane_read(L.scales1, f.s), lane_read(L.scales0, f.s), L.sel);
+    return o;
 }
 
 template <int MT, int NT>
@@ -94,8 +132,9 @@ __device__ __forceinline__ void load_full_chunk(Frags<MT, NT>& f, const uint8_t*
     for (int u = 0; u < MT; ++u) load_full(ac[u], as[u], c, f.a[u]);
 }
 
+// One chunk's MT x NT tiles from fragments in the operand layout.
 template <int MT, int NT>
-__device__ __forceinline__ void compute_frags(const RowFrag (&w)[NT], const RowFrag (&a)[MT], f32x4 (&acc)[NT][MT]) {
+__device__ __forceinline__ void mma_chunk(const RowFrag (&w)[NT], const RowFrag (&a)[MT], f32x4 (&acc)[NT][MT]) {
     half2_t sw[NT][2], sa[MT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -123,9 +162,15 @@ __device__ __forceinline__ void compute_frags(const RowFrag (&w)[NT], const RowF
     }
 }
 
+// One chunk's tiles from fragments in the load layout.
 template <int MT, int NT>
-__device__ __forceinline__ void compute_chunk(const Frags<MT, NT>& f, f32x4 (&acc)[NT][MT]) {
-    compute_frags<MT, NT>(f.w, f.a, acc);
+__device__ __forceinline__ void compute_chunk(const Frags<MT, NT>& f, const OperandLanes& L, f32x4 (&acc)[NT][MT]) {
+    RowFrag w[NT], a[MT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t] = to_operand(f.w[t], L);
+#pragma unroll
+    for (int u = 0; u < MT; ++u) a[u] = to_operand(f.a[u], L);
+    mma_chunk<MT, NT>(w, a, acc);
 }
 
 template <int MT, int NT>
@@ -135,7 +180,8 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
     int64_t M, int64_t N, int64_t K, const SegParams sp) {
     extern __shared__ float red[];  // [KW][NT][MT][4][64] partial sums
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kw = blockDim.x >> 6;
-    const int r = lane & 15, g = lane >> 4;
+    const int rl = lane >> 2, q = lane & 3;  // the row this lane loads, its piece
+    const OperandLanes L = operand_lanes(lane);
     const int64_t n0 = (int64_t)blockIdx.x * (16 * NT);
 
     // rows past N or M are clamped to the last row: their results are never stored
@@ -145,15 +191,15 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
     const uint8_t* as[MT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int64_t n = std::min<int64_t>(n0 + 16 * t + r, N - 1);
-        wc[t] = w_codes + n * ldw_c + 32 * g;
-        ws[t] = w_scales + n * ldw_s + 4 * g;
+        const int64_t n = std::min<int64_t>(n0 + 16 * t + rl, N - 1);
+        wc[t] = w_codes + n * ldw_c + 16 * q;
+        ws[t] = w_scales + n * ldw_s + 4 * q;
     }
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-        const int64_t m = std::min<int64_t>(16 * u + r, M - 1);
-        ac[u] = a_codes + m * lda_c + 32 * g;
-        as[u] = a_scales + m * lda_s + 4 * g;
+        const int64_t m = std::min<int64_t>(16 * u + rl, M - 1);
+        ac[u] = a_codes + m * lda_c + 16 * q;
+        as[u] = a_scales + m * lda_s + 4 * q;
     }
 
     const int64_t nch = (K + CHUNK - 1) / CHUNK, nfull = K / CHUNK;
@@ -183,23 +229,23 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
                 load_full_chunk<MT, NT>(f[(i + DEPTH) % RING], wc, ws, ac, as, std::min(c + i + DEPTH, c_end - 1));
                 // keep the loads ahead of this chunk's arithmetic: sunk below it they would be waited for
                 __builtin_amdgcn_sched_barrier(0);
-                compute_chunk<MT, NT>(f[i], acc);
+                compute_chunk<MT, NT>(f[i], L, acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // fewer than RING chunks left, already loaded into f[0 ..]
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i)
-            if (c + i < c_end) compute_chunk<MT, NT>(f[i], acc);
+            if (c + i < c_end) compute_chunk<MT, NT>(f[i], L, acc);
     }
     // the chunk that crosses K, if any, is the last chunk of the last wave
     if (c_hi > nfull && c_lo <= nfull) {
         Frags<MT, NT> t;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) load_tail(wc[i], ws[i], nfull, g, K, t.w[i]);
+        for (int i = 0; i < NT; ++i) load_tail(wc[i], ws[i], nfull, q, K, t.w[i]);
 #pragma unroll
-        for (int u = 0; u < MT; ++u) load_tail(ac[u], as[u], nfull, g, K, t.a[u]);
-        compute_chunk<MT, NT>(t, acc);
+        for (int u = 0; u < MT; ++u) load_tail(ac[u], as[u], nfull, q, K, t.a[u]);
+        compute_chunk<MT, NT>(t, L, acc);
     }
 
     constexpr int TILE = NT * MT * 256;
@@ -268,15 +314,18 @@ constexpr int WIDE_SLOTS = 3;                // register ring: K-group chunk i i
 constexpr int WIDE_KG = 2;                   // K-groups of 4 waves per workgroup
 
 // One K-group's FP16 activation chunk: [tile u][step j][lane] -> the 8 values lane (g, r) feeds at
-// step j for activation row 16u + r (elements 64g + 8j .. + 7 of the chunk). A K-group of WPG waves
+// step j for activation row 16u + r (elements 128 (j / 4) + 32g + 8 (j % 4) .. + 7 of the chunk, the
+// operand layout of RowFrag). A K-group of WPG waves
 // has WPG tiles: tiles 0-3 hold the (at most 64) activation rows; a fifth wave's tile is written and
 // never read.
 template <int WPG>
 using ActChunk = half8_t[WPG][8][64];
 
-// Lane (g, r) of wave u converts its fragment of activation row 16u + r into the chunk.
+// Lane (g, r) of wave u converts its fragment of activation row 16u + r into the chunk (loaded in
+// the load layout; moved to the operand layout here).
 template <int WPG>
-__device__ __forceinline__ void stage_act(ActChunk<WPG>& dst, const RowFrag& f, int u, int lane) {
+__device__ __forceinline__ void stage_act(ActChunk<WPG>& dst, const RowFrag& fl, int u, int lane) {
+    const RowFrag f = to_operand(fl, operand_lanes(lane));
     half2_t sa[2];
     sa[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
     sa[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
@@ -286,9 +335,13 @@ __device__ __forceinline__ void stage_act(ActChunk<WPG>& dst, const RowFrag& f, 
 
 // The MT x NT tiles of one chunk: weights dequantized here, activations read from the chunk.
 template <int MT, int NT, int WPG>
-__device__ __forceinline__ void compute_lds(const RowFrag (&w)[NT], const ActChunk<WPG>& act, int lane,
+__device__ __forceinline__ void compute_lds(const RowFrag (&wl)[NT], const ActChunk<WPG>& act, int lane,
                                             f32x4 (&acc)[NT][MT]) {
     constexpr int WIDE_NT = NT;
+    RowFrag w[WIDE_NT];
+    const OperandLanes L = operand_lanes(lane);
+#pragma unroll
+    for (int t = 0; t < WIDE_NT; ++t) w[t] = to_operand(wl[t], L);
     half2_t sw[WIDE_NT][2];
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) {
@@ -354,7 +407,8 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
     __shared__ ActChunk<WPG> lds[WIDE_KG][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = wave / WPG, u = wave % WPG;
-    const int r = lane & 15, g = lane >> 4;
+    const int r = lane & 15, g = lane >> 4;  // the operand layout (results)
+    const int rl = lane >> 2, q = lane & 3;   // the load layout: the row this lane loads, its piece
     const int64_t groups = (N + WIDE_ROWS - 1) / WIDE_ROWS;
     const int64_t grp = blockIdx.x % groups;
     const int split = (int)(blockIdx.x / groups);
@@ -366,13 +420,13 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
     const uint8_t* ws[WIDE_NT];
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) {
-        const int64_t n = std::min<int64_t>(n0 + 16 * t + r, N - 1);
-        wc[t] = w_codes + n * ldw_c + 32 * g;
-        ws[t] = w_scales + n * ldw_s + 4 * g;
+        const int64_t n = std::min<int64_t>(n0 + 16 * t + rl, N - 1);
+        wc[t] = w_codes + n * ldw_c + 16 * q;
+        ws[t] = w_scales + n * ldw_s + 4 * q;
     }
-    const int64_t arow = std::min<int64_t>(16 * u + r, M - 1);
-    const uint8_t* ac = a_codes + arow * lda_c + 32 * g;
-    const uint8_t* as = a_scales + arow * lda_s + 4 * g;
+    const int64_t arow = std::min<int64_t>(16 * u + rl, M - 1);
+    const uint8_t* ac = a_codes + arow * lda_c + 16 * q;
+    const uint8_t* as = a_scales + arow * lda_s + 4 * q;
 
     const int64_t nch = (K + CHUNK - 1) / CHUNK, nfull = K / CHUNK;
     const int64_t c_lo = std::min<int64_t>(nch, split * per), c_hi = std::min<int64_t>(nch, c_lo + per);
@@ -419,9 +473,9 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
         RowFrag twf[WIDE_NT];
         if (kg == 0) {
             RowFrag taf;
-            load_tail(ac, as, c_fhi, g, K, taf);
+            load_tail(ac, as, c_fhi, q, K, taf);
 #pragma unroll
-            for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, g, K, twf[t]);
+            for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, q, K, twf[t]);
             stage_act<WPG>(act[0], taf, u, lane);
         }
         __syncthreads();
