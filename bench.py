@@ -197,6 +197,12 @@ def time_quantizer_rotating(step: Step, copies: int = 3, reps: int = 10) -> dict
     return {"ms": ms, "rotation_bytes": in_bytes, "copies": copies, "launches": reps * copies}
 
 
+def decode_kernel_name(M: int, K: int) -> str:
+    """The kernel the library runs for M <= 32 activation rows: the weight-streaming GEMV for one row
+    (K from 16 to 32768), else the skinny kernel."""
+    return "gemm_gemv_kernel" if M == 1 and 16 <= K <= 32768 else "gemm_skinny_kernel"
+
+
 def gemm_roofline(case: wl.GemmCase, ms: float) -> dict:
     """TFLOP/s, GB/s and the roofline the GEMM of `case` runs against: the dense FP16 MFMA peak above
     the ridge point (peak FLOP/s per HBM byte/s), HBM bandwidth below it."""
@@ -217,7 +223,7 @@ def gemm_roofline(case: wl.GemmCase, ms: float) -> dict:
         kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if nv.lib().nvfp4_gemm_workspace_bytes(M, N, K)
                                        else "")
     else:
-        kernel = "gemm_skinny_kernel"
+        kernel = decode_kernel_name(M, K)
     roof.update({"kernel": kernel, "avg_ms": ms, "algorithmic_flop": flops, "algorithmic_bytes": nbytes})
     return {"ms": ms, "tflops": tflops, "gbps": gbps, "roofline": roof}
 
@@ -689,7 +695,7 @@ def main() -> int:
     elif M > 32:  # the reduce kernel runs only when K is split over workgroups (the workspace holds the parts)
         kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if step.workspace is not None else "")
     else:
-        kernel = "gemm_skinny_kernel"
+        kernel = decode_kernel_name(M, K)
     tr = measured_traffic(kernel, case.name)
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,
