@@ -104,27 +104,32 @@ __global__ __launch_bounds__(256) void fold_scales_kernel(uint8_t* __restrict__ 
 // Lane l owns the 16-element blocks l, l + 64, ... of its row. With NBL > 0 (rows of at most
 // 64 * NBL blocks) the row stays in registers between the sum and the encoding, so it is read
 // once; NBL == 0 handles any K with a second pass over the row, which finds it in L2.
-__device__ __forceinline__ double sum_squares16(const qu32x4& p0, const qu32x4& p1) {
+
+// The block's 16 elements widened to FP32 (exact), in order.
+__device__ __forceinline__ void widen16(const qu32x4& p0, const qu32x4& p1, float (&xf)[16]) {
     const uint32_t wv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const double lo = bf16_lo(wv[i]), hi = bf16_hi(wv[i]);
-        ss += lo * lo;
-        ss += hi * hi;
+        xf[2 * i] = bf16_lo(wv[i]);
+        xf[2 * i + 1] = bf16_hi(wv[i]);
     }
+}
+
+__device__ __forceinline__ double sum_squares_f(const float (&xf)[16]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += (double)xf[i] * (double)xf[i];
     return ss;
 }
 
-// wf: the block's 16 norm weights as FP32 (exact bf16 values).
-__device__ __forceinline__ void norm_encode_block(const qu32x4& p0, const qu32x4& p1, const float* wf, int64_t b,
-                                                  float r, float g, uint8_t* __restrict__ codes_row,
-                                                  uint8_t* __restrict__ scales_row, uint16_t* __restrict__ y_row) {
-    const uint32_t xv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+// xf: the block's 16 elements as FP32; wf: its 16 norm weights as FP32 (exact bf16 values).
+__device__ __forceinline__ void norm_encode_block(const float (&xf)[16], const float* wf, int64_t b, float r, float g,
+                                                  uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
+                                                  uint16_t* __restrict__ y_row) {
     float f[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {  // two elements per bf16 rounding instruction
-        const uint32_t y1 = bf16x2_rne(bf16_lo(xv[i]) * r, bf16_hi(xv[i]) * r);
+        const uint32_t y1 = bf16x2_rne(xf[2 * i] * r, xf[2 * i + 1] * r);
         const uint32_t y = bf16x2_rne(bf16_lo(y1) * wf[2 * i], bf16_hi(y1) * wf[2 * i + 1]);
         f[2 * i] = bf16_lo(y);
         f[2 * i + 1] = bf16_hi(y);
@@ -195,21 +200,28 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
         }
         __syncthreads();
         if (row >= rows) return;
+        // the elements are widened once, for the sum and for the norm
+        float xf[NBL][16];
         double ss = 0.0;
 #pragma unroll
         for (int j = 0; j < NBL; ++j)
-            if (lane + 64 * j < nb) ss += sum_squares16(p[j][0], p[j][1]);
+            if (lane + 64 * j < nb) {
+                widen16(p[j][0], p[j][1], xf[j]);
+                ss += sum_squares_f(xf[j]);
+            }
         const float r = row_rscale(ss, K, eps);
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int64_t b = lane + 64 * j;
-            if (b < nb) norm_encode_block(p[j][0], p[j][1], w_lds + 16 * b, b, r, g, codes_row, scales_row, y_row);
+            if (b < nb) norm_encode_block(xf[j], w_lds + 16 * b, b, r, g, codes_row, scales_row, y_row);
         }
     } else {
         double ss = 0.0;
         for (int64_t b = lane; b < nb; b += 64) {
             const qu32x4* src = reinterpret_cast<const qu32x4*>(xr + 16 * b);
-            ss += sum_squares16(src[0], src[1]);
+            float xf[16];
+            widen16(src[0], src[1], xf);
+            ss += sum_squares_f(xf);
         }
         const float r = row_rscale(ss, K, eps);
         for (int64_t b = lane; b < nb; b += 64) {
@@ -224,7 +236,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quantize_kernel(
                 wf[8 + 2 * i] = bf16_lo(w1[i]);
                 wf[8 + 2 * i + 1] = bf16_hi(w1[i]);
             }
-            norm_encode_block(src[0], src[1], wf, b, r, g, codes_row, scales_row, y_row);
+            float xf[16];
+            widen16(src[0], src[1], xf);
+            norm_encode_block(xf, wf, b, r, g, codes_row, scales_row, y_row);
         }
     }
 }
