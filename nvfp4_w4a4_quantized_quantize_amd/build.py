@@ -94,7 +94,7 @@ def build(verbose: bool = False, jobs: int | None = None, extra: list[str] | Non
 
 def built_from_current_sources(lib: str, srcs: list[str]) -> bool:
     """True when ``lib`` exists and the digest written beside it at build time matches the sources
-    as they are now (content, not modification times, so copies of the tree keep their verdict)."""
+    as they are now (content, not modification times, so copies of the tree give the same answer)."""
     try:
         with open(lib + ".digest") as fh:
             return os.path.exists(lib) and fh.read().strip() == digest(srcs)
