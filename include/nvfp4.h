@@ -173,6 +173,44 @@ nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a_codes, int64_t lda_c, const uin
                                 const uint8_t* w_scales, int64_t ldw_s, int64_t M, int64_t N, int64_t K,
                                 const nvfp4_segment* segs, const float* g_w, int32_t n_segs, void* stream);
 
+/*
+ * Decode weight layout -- NVFP4 weights repacked once, offline, for the decode GEMMs (M <= 64), where
+ * the weights are nearly all of the traffic (Japanese article, "Running 27B at home": decode is
+ * weight streaming). With T = ceil(N / 16) tiles of 16 rows and C = ceil(K / 256) chunks of 256
+ * elements, tile t and chunk c hold:
+ *   codes  at (t C + c) * 2048: piece h = 0, 1 of 1024 bytes; within a piece, 16 bytes per lane
+ *          l = r + 16 g (r < 16, g < 4): code bytes 64 h + 16 g .. + 15 of chunk c of row 16 t + r;
+ *   scales at T C 2048 + (t C + c) * 256: 4 bytes per lane l: the E4M3 scale bytes of blocks
+ *          2g, 2g + 1, 8 + 2g, 9 + 2g of chunk c of row 16 t + r.
+ * Codes and scales are those of the row-major weights, moved; rows past N and bytes past K are zero.
+ * In this order each load of the decode kernels is one contiguous run and needs no lane exchange.
+ */
+
+/* Bytes of the decode layout of N x K weights: T * C * 2304 (0 when N <= 0, K <= 0 or K % 16 != 0). */
+size_t nvfp4_packed_weight_bytes(int64_t N, int64_t K);
+
+/*
+ * nvfp4_pack_weights -- write the decode layout of row-major NVFP4 weights (codes [N, K/2] stride
+ * ldw_c, scales [N, K/16] stride ldw_s, as for nvfp4_gemm) into packed: a device buffer of
+ * nvfp4_packed_weight_bytes(N, K) bytes, 16-byte aligned, owned by the caller. N == 0 or K == 0 is a
+ * no-op. Errors: NULL, SHAPE, ALIGN, HIP.
+ */
+nvfp4_status nvfp4_pack_weights(const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                                int64_t N, int64_t K, uint8_t* packed, void* stream);
+
+/*
+ * nvfp4_gemm_packed -- nvfp4_gemm for 1 <= M <= 64 activation rows with weights in the decode layout
+ * (w_packed from nvfp4_pack_weights for the same N and K). Same activations, segments, global scales,
+ * epilogues and workspace (nvfp4_gemm_workspace_bytes) as nvfp4_gemm; for 2 <= M <= 64 the results
+ * are bitwise those of nvfp4_gemm with the row-major weights (same kernels, same order of every sum).
+ * At M = 1 nvfp4_gemm streams whole row-major rows and is the faster of the two.
+ * M > 64: NVFP4_ERR_SHAPE (the prefill kernel reads row-major weights). Errors: as nvfp4_gemm.
+ */
+nvfp4_status nvfp4_gemm_packed(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                               float g_a, const uint8_t* w_packed, int64_t M, int64_t N, int64_t K,
+                               const nvfp4_segment* segs, const float* g_w, int32_t n_segs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Companions on the same serving path
  * --------------------------------------------------------------------------------------------- */

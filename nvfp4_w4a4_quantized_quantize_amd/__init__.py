@@ -33,7 +33,8 @@ _EPI = {"none": EPI_NONE, "sigmoid": EPI_SIGMOID, "gdn_decay": EPI_GDN_DECAY}
 EXPORTED = ("nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_workspace_bytes",
             "nvfp4_status_string", "nvfp4_last_error", "nvfp4_kv_scale", "nvfp4_kv_quantize",
             "nvfp4_kv_dequantize", "nvfp4_fold_scales", "nvfp4_fold_group", "nvfp4_rmsnorm_quantize",
-            "nvfp4_gdn_recurrence", "nvfp4_gdn_workspace_bytes", "nvfp4_gemm_noalloc")
+            "nvfp4_gdn_recurrence", "nvfp4_gdn_workspace_bytes", "nvfp4_gemm_noalloc",
+            "nvfp4_packed_weight_bytes", "nvfp4_pack_weights", "nvfp4_gemm_packed")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -76,6 +77,13 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(_Segment), ctypes.POINTER(f32), i32, P]
         L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_packed_weight_bytes.restype = ctypes.c_size_t
+        L.nvfp4_packed_weight_bytes.argtypes = [i64, i64]
+        L.nvfp4_pack_weights.restype = i32
+        L.nvfp4_pack_weights.argtypes = [P, i64, P, i64, i64, i64, P, P]
+        L.nvfp4_gemm_packed.restype = i32
+        L.nvfp4_gemm_packed.argtypes = [P, i64, P, i64, f32, P, i64, i64, i64,
+                                        ctypes.POINTER(_Segment), ctypes.POINTER(f32), i32, P, ctypes.c_size_t, P]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         L.nvfp4_status_string.argtypes = [i32]
         L.nvfp4_last_error.restype = ctypes.c_char_p
@@ -221,6 +229,40 @@ def gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_codes: tor
     _check(lib().nvfp4_gemm(_ptr(a_codes), _ld(a_codes, 16), _ptr(a_scales), _ld(a_scales, 16), float(g_a),
                             _ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), M, N, K,
                             segs, g_w, n_segs, _ptr(workspace), ws_bytes, _stream(stream)), "nvfp4_gemm")
+    return outs
+
+
+def pack_weights(w_codes: torch.Tensor, w_scales: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """The decode layout of NVFP4 weights (codes [N, K/2], scales [N, K/16]) for gemm_packed: a uint8
+    device tensor of nvfp4_packed_weight_bytes(N, K) bytes (a preallocated one may be passed)."""
+    N, K = w_codes.shape[0], w_codes.shape[1] * 2
+    assert w_scales.shape == (N, K // 16)
+    need = lib().nvfp4_packed_weight_bytes(N, K)
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device=w_codes.device)
+    assert out.numel() * out.element_size() >= need
+    _check(lib().nvfp4_pack_weights(_ptr(w_codes), _ld(w_codes, 16), _ptr(w_scales), _ld(w_scales, 16), N, K,
+                                    _ptr(out), _stream(stream)), "nvfp4_pack_weights")
+    return out
+
+
+def gemm_packed(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: float, w_packed: torch.Tensor, N: int,
+                segments: Sequence[Segment], workspace: Optional[torch.Tensor] = None,
+                stream=None) -> list[torch.Tensor]:
+    """gemm() for M <= 64 activation rows with weights in the decode layout (pack_weights of the N x K
+    weights, K from the activations). Returns one output tensor [M, n_s] per segment."""
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    assert a_scales.shape == (M, K // 16)
+    assert w_packed.numel() * w_packed.element_size() >= lib().nvfp4_packed_weight_bytes(N, K)
+    segs, g_w, n_segs, outs = _segments(a_codes, M, N, segments)
+    need = lib().nvfp4_gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvfp4_gemm_packed(_ptr(a_codes), _ld(a_codes, 16), _ptr(a_scales), _ld(a_scales, 16), float(g_a),
+                                   _ptr(w_packed), M, N, K, segs, g_w, n_segs, _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "nvfp4_gemm_packed")
     return outs
 
 

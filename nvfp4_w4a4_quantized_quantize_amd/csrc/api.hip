@@ -146,19 +146,30 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t K, int64_t
 
 namespace {
 
-// Validation and launch of nvfp4_gemm and nvfp4_gemm_noalloc. With noalloc the workspace arguments
-// are ignored: the partial sums go to the current device's scratch array.
+// Validation and launch of nvfp4_gemm, nvfp4_gemm_noalloc and nvfp4_gemm_packed. With noalloc the
+// workspace arguments are ignored: the partial sums go to the current device's scratch array. With
+// packed the weights are w_packed, in the decode layout, and w_codes .. ldw_s are unused.
 nvfp4_status gemm_entry(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s, float g_a,
-                        const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, int64_t M,
-                        int64_t N, int64_t K, const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
-                        void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
+                        const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, bool packed,
+                        const uint8_t* w_packed, int64_t M, int64_t N, int64_t K, const nvfp4_segment* segs,
+                        const float* g_w, int32_t n_segs, void* workspace, size_t workspace_bytes, bool noalloc,
+                        void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
     if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return fail(NVFP4_ERR_SHAPE, "M or N too large");
+    if (packed && M > nvfp4::SKINNY_MAX_M)
+        return fail(NVFP4_ERR_SHAPE, "packed weights serve M <= %lld activation rows, M = %lld",
+                    (long long)nvfp4::SKINNY_MAX_M, (long long)M);
     nvfp4_status st = check_nvfp4(a_codes, lda_c, a_scales, lda_s, M, K, "A");
     if (st != NVFP4_OK) return st;
-    st = check_nvfp4(w_codes, ldw_c, w_scales, ldw_s, N, K, "W");
-    if (st != NVFP4_OK) return st;
+    if (packed) {
+        if (M > 0 && N > 0 && K > 0 && !w_packed) return fail(NVFP4_ERR_NULL, "w_packed is NULL");
+        if (!aligned16(w_packed)) return fail(NVFP4_ERR_ALIGN, "packed weights must be 16-byte aligned");
+        ldw_c = ldw_s = 0;
+    } else {
+        st = check_nvfp4(w_codes, ldw_c, w_scales, ldw_s, N, K, "W");
+        if (st != NVFP4_OK) return st;
+    }
     // the prefill kernel addresses a 256-row tile of each operand with 32-bit buffer offsets
     if (lda_c >= MAX_GEMM_LD || lda_s >= MAX_GEMM_LD || ldw_c >= MAX_GEMM_LD || ldw_s >= MAX_GEMM_LD)
         return fail(NVFP4_ERR_SHAPE, "row strides must be below %lld bytes", (long long)MAX_GEMM_LD);
@@ -230,16 +241,26 @@ nvfp4_status gemm_entry(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     }
     const hipStream_t st_ = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (packed) {
+        const uint8_t* ps = nvfp4::packed_scales(w_packed, N, K);
+        if (M > nvfp4::SKINNY_NARROW_M)
+            e = nvfp4::launch_gemm_wide(a_codes, lda_c, a_scales, lda_s, w_packed, 0, ps, 0, M, N, K, sp, workspace,
+                                        true, st_);
+        else
+            e = nvfp4::launch_gemm_skinny(a_codes, lda_c, a_scales, lda_s, w_packed, 0, ps, 0, M, N, K, sp, true,
+                                          st_);
+        return hip_status(e, "nvfp4_gemm_packed launch");
+    }
     if (M > nvfp4::SKINNY_MAX_M)
         e = nvfp4::launch_gemm_tiled(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp, st_);
     else if (M > nvfp4::SKINNY_NARROW_M)
         e = nvfp4::launch_gemm_wide(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
-                                    workspace, st_);
+                                    workspace, false, st_);
     else if (nvfp4::gemv_supported(M, K))
         e = nvfp4::launch_gemm_gemv(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp, st_);
     else
         e = nvfp4::launch_gemm_skinny(a_codes, lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, sp,
-                                      st_);
+                                      false, st_);
     return hip_status(e, noalloc ? "nvfp4_gemm_noalloc launch" : "nvfp4_gemm launch");
 }
 
@@ -251,16 +272,44 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
                         const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s, int64_t M,
                         int64_t N, int64_t K, const nvfp4_segment* segs, const float* g_w, int32_t n_segs,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, M, N, K, segs, g_w, n_segs,
-                      workspace, workspace_bytes, false, stream);
+    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, false, nullptr, M, N, K,
+                      segs, g_w, n_segs, workspace, workspace_bytes, false, stream);
+}
+
+size_t nvfp4_packed_weight_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % 16 != 0) return 0;
+    return nvfp4::packed_weight_bytes(N, K);
+}
+
+nvfp4_status nvfp4_pack_weights(const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                                int64_t N, int64_t K, uint8_t* packed, void* stream) {
+    if (N < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+    if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
+    if (N > (int64_t)1 << 31) return fail(NVFP4_ERR_SHAPE, "N too large");
+    nvfp4_status st = check_nvfp4(w_codes, ldw_c, w_scales, ldw_s, N, K, "W");
+    if (st != NVFP4_OK) return st;
+    if (N == 0 || K == 0) return ok();
+    if (!packed) return fail(NVFP4_ERR_NULL, "packed is NULL");
+    if (!aligned16(packed)) return fail(NVFP4_ERR_ALIGN, "packed must be 16-byte aligned");
+    return hip_status(nvfp4::launch_pack_weights(w_codes, ldw_c, w_scales, ldw_s, N, K, packed,
+                                                 static_cast<hipStream_t>(stream)),
+                      "nvfp4_pack_weights launch");
+}
+
+nvfp4_status nvfp4_gemm_packed(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
+                               float g_a, const uint8_t* w_packed, int64_t M, int64_t N, int64_t K,
+                               const nvfp4_segment* segs, const float* g_w, int32_t n_segs, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, nullptr, 0, nullptr, 0, true, w_packed, M, N, K, segs, g_w,
+                      n_segs, workspace, workspace_bytes, false, stream);
 }
 
 nvfp4_status nvfp4_gemm_noalloc(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                                 float g_a, const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales,
                                 int64_t ldw_s, int64_t M, int64_t N, int64_t K, const nvfp4_segment* segs,
                                 const float* g_w, int32_t n_segs, void* stream) {
-    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, M, N, K, segs, g_w, n_segs,
-                      nullptr, 0, true, stream);
+    return gemm_entry(a_codes, lda_c, a_scales, lda_s, g_a, w_codes, ldw_c, w_scales, ldw_s, false, nullptr, M, N, K,
+                      segs, g_w, n_segs, nullptr, 0, true, stream);
 }
 
 nvfp4_status nvfp4_kv_scale(const void* x_bf16, int64_t rows, int64_t cols, int64_t ldx, float* s_out,

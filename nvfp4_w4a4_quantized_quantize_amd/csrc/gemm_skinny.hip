@@ -116,18 +116,74 @@ __device__ __forceinline__ RowFrag to_operand(const RowFrag& f, const OperandLan
     return o;
 }
 
+// The decode weight layout (nvfp4_pack_weights): 16-row tiles by 256-element chunks. Tile t, chunk c
+// (of C = ceil(K / 256)) holds at (t C + c) * PK_CODES its two 1 KB code pieces already in the
+// operand layout (piece h, lane r + 16g: row 16t + r, code bytes 64h + 16g .. + 15 of the chunk) and,
+// after all T C of those, at (t C + c) * PK_SCALES its scale dwords (lane r + 16g: scale bytes 2g,
+// 2g + 1, 8 + 2g, 9 + 2g of that row and chunk). Rows past N and bytes past K are zero, so a padded
+// block has a zero scale and adds exact zeros, and the chunk that crosses K needs no special load.
+// Every load of a packed operand is one contiguous 1 KB (or 256-byte) run.
+constexpr int PK_CODES = 2048, PK_SCALES = 256;
+
+// codes/scales point at the lane's bytes of chunk 0 of its tile (tile base + 16 lane, + 4 lane).
+__device__ __forceinline__ void load_packed(const uint8_t* codes, const uint8_t* scales, int64_t c, RowFrag& f) {
+    const uint8_t* p = codes + c * PK_CODES;
+    f.c[0] = *reinterpret_cast<const u32x4*>(p);
+    f.c[1] = *reinterpret_cast<const u32x4*>(p + 1024);
+    f.s = *reinterpret_cast<const uint32_t*>(scales + c * PK_SCALES);
+}
+
+// A weight fragment of chunk c (the chunk that crosses K when tail): packed weights are loaded in the
+// operand layout, row-major ones in the load layout.
+template <bool PK>
+__device__ __forceinline__ void load_w(const uint8_t* codes, const uint8_t* scales, int64_t c, bool tail, int q,
+                                       int64_t K, RowFrag& f) {
+    if constexpr (PK)
+        load_packed(codes, scales, c, f);
+    else if (tail)
+        load_tail(codes, scales, c, q, K, f);
+    else
+        load_full(codes, scales, c, f);
+}
+
+template <bool PK>
+__device__ __forceinline__ RowFrag w_operand(const RowFrag& f, const OperandLanes& L) {
+    if constexpr (PK)
+        return f;
+    else
+        return to_operand(f, L);
+}
+
+// The lane's weight pointers for weight rows n0 .. n0 + 15 (rows past N clamped to the last row; for
+// packed weights, tiles past the last clamped to it): row-major in the load layout, or packed.
+template <bool PK>
+__device__ __forceinline__ void w_pointers(const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales,
+                                           int64_t ldw_s, int64_t n0, int64_t N, int64_t K, int lane,
+                                           const uint8_t*& wc, const uint8_t*& ws) {
+    if constexpr (PK) {
+        const int64_t C = (K + CHUNK - 1) / CHUNK;
+        const int64_t tile = std::min<int64_t>(n0 / 16, (N - 1) / 16);
+        wc = w_codes + tile * C * PK_CODES + 16 * lane;
+        ws = w_scales + tile * C * PK_SCALES + 4 * lane;
+    } else {
+        const int64_t n = std::min<int64_t>(n0 + (lane >> 2), N - 1);
+        wc = w_codes + n * ldw_c + 16 * (lane & 3);
+        ws = w_scales + n * ldw_s + 4 * (lane & 3);
+    }
+}
+
 template <int MT, int NT>
 struct Frags {
     RowFrag w[NT];
     RowFrag a[MT];
 };
 
-template <int MT, int NT>
+template <int MT, int NT, bool PK>
 __device__ __forceinline__ void load_full_chunk(Frags<MT, NT>& f, const uint8_t* const (&wc)[NT],
                                                 const uint8_t* const (&ws)[NT], const uint8_t* const (&ac)[MT],
                                                 const uint8_t* const (&as)[MT], int64_t c) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_full(wc[t], ws[t], c, f.w[t]);
+    for (int t = 0; t < NT; ++t) load_w<PK>(wc[t], ws[t], c, false, 0, 0, f.w[t]);
 #pragma unroll
     for (int u = 0; u < MT; ++u) load_full(ac[u], as[u], c, f.a[u]);
 }
@@ -162,18 +218,18 @@ __device__ __forceinline__ void mma_chunk(const RowFrag (&w)[NT], const RowFrag 
     }
 }
 
-// One chunk's tiles from fragments in the load layout.
-template <int MT, int NT>
+// One chunk's tiles from fragments as loaded (activations in the load layout).
+template <int MT, int NT, bool PK>
 __device__ __forceinline__ void compute_chunk(const Frags<MT, NT>& f, const OperandLanes& L, f32x4 (&acc)[NT][MT]) {
     RowFrag w[NT], a[MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[t] = to_operand(f.w[t], L);
+    for (int t = 0; t < NT; ++t) w[t] = w_operand<PK>(f.w[t], L);
 #pragma unroll
     for (int u = 0; u < MT; ++u) a[u] = to_operand(f.a[u], L);
     mma_chunk<MT, NT>(w, a, acc);
 }
 
-template <int MT, int NT>
+template <int MT, int NT, bool PK>
 __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
     const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
@@ -190,11 +246,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
     const uint8_t* ac[MT];
     const uint8_t* as[MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int64_t n = std::min<int64_t>(n0 + 16 * t + rl, N - 1);
-        wc[t] = w_codes + n * ldw_c + 16 * q;
-        ws[t] = w_scales + n * ldw_s + 4 * q;
-    }
+    for (int t = 0; t < NT; ++t) w_pointers<PK>(w_codes, ldw_c, w_scales, ldw_s, n0 + 16 * t, N, K, lane, wc[t], ws[t]);
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
         const int64_t m = std::min<int64_t>(16 * u + rl, M - 1);
@@ -221,31 +273,31 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
         constexpr int RING = DEPTH + 1;
         Frags<MT, NT> f[RING];
 #pragma unroll
-        for (int i = 0; i < DEPTH; ++i) load_full_chunk<MT, NT>(f[i], wc, ws, ac, as, std::min(c_lo + i, c_end - 1));
+        for (int i = 0; i < DEPTH; ++i) load_full_chunk<MT, NT, PK>(f[i], wc, ws, ac, as, std::min(c_lo + i, c_end - 1));
         int64_t c = c_lo;
         for (; c + RING <= c_end; c += RING) {
 #pragma unroll
             for (int i = 0; i < RING; ++i) {
-                load_full_chunk<MT, NT>(f[(i + DEPTH) % RING], wc, ws, ac, as, std::min(c + i + DEPTH, c_end - 1));
+                load_full_chunk<MT, NT, PK>(f[(i + DEPTH) % RING], wc, ws, ac, as, std::min(c + i + DEPTH, c_end - 1));
                 // keep the loads ahead of this chunk's arithmetic: sunk below it they would be waited for
                 __builtin_amdgcn_sched_barrier(0);
-                compute_chunk<MT, NT>(f[i], L, acc);
+                compute_chunk<MT, NT, PK>(f[i], L, acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // fewer than RING chunks left, already loaded into f[0 ..]
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i)
-            if (c + i < c_end) compute_chunk<MT, NT>(f[i], L, acc);
+            if (c + i < c_end) compute_chunk<MT, NT, PK>(f[i], L, acc);
     }
     // the chunk that crosses K, if any, is the last chunk of the last wave
     if (c_hi > nfull && c_lo <= nfull) {
         Frags<MT, NT> t;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) load_tail(wc[i], ws[i], nfull, q, K, t.w[i]);
+        for (int i = 0; i < NT; ++i) load_w<PK>(wc[i], ws[i], nfull, true, q, K, t.w[i]);
 #pragma unroll
         for (int u = 0; u < MT; ++u) load_tail(ac[u], as[u], nfull, q, K, t.a[u]);
-        compute_chunk<MT, NT>(t, L, acc);
+        compute_chunk<MT, NT, PK>(t, L, acc);
     }
 
     constexpr int TILE = NT * MT * 256;
@@ -280,9 +332,9 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void gemm_skinny_kernel(
 typedef void (*skinny_fn)(const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*,
                           int64_t, int64_t, int64_t, int64_t, const SegParams);
 
-template <int MT>
+template <int MT, bool PK>
 skinny_fn pick_nt(int nt) {
-    return nt >= 2 ? gemm_skinny_kernel<MT, 2> : gemm_skinny_kernel<MT, 1>;
+    return nt >= 2 ? gemm_skinny_kernel<MT, 2, PK> : gemm_skinny_kernel<MT, 1, PK>;
 }
 
 // Waves per workgroup splitting K: depends on K alone, so the order of the additions (and so every
@@ -334,14 +386,14 @@ __device__ __forceinline__ void stage_act(ActChunk<WPG>& dst, const RowFrag& fl,
 }
 
 // The MT x NT tiles of one chunk: weights dequantized here, activations read from the chunk.
-template <int MT, int NT, int WPG>
+template <int MT, int NT, int WPG, bool PK>
 __device__ __forceinline__ void compute_lds(const RowFrag (&wl)[NT], const ActChunk<WPG>& act, int lane,
                                             f32x4 (&acc)[NT][MT]) {
     constexpr int WIDE_NT = NT;
     RowFrag w[WIDE_NT];
     const OperandLanes L = operand_lanes(lane);
 #pragma unroll
-    for (int t = 0; t < WIDE_NT; ++t) w[t] = to_operand(wl[t], L);
+    for (int t = 0; t < WIDE_NT; ++t) w[t] = w_operand<PK>(wl[t], L);
     half2_t sw[WIDE_NT][2];
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) {
@@ -368,7 +420,7 @@ __device__ __forceinline__ void compute_lds(const RowFrag (&wl)[NT], const ActCh
 // convert the activations of chunk i + 1 into the other buffer. A chunk index at or past c_fhi (a
 // repeat of the last full chunk) gets zero weight scales, which adds exact zeros. There is no branch
 // in here: a load under one is issued where its value is used, or waited for at the join.
-template <int MT, int NT, int WPG, bool LOADS>
+template <int MT, int NT, int WPG, bool PK, bool LOADS>
 __device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c_fhi, int64_t cl,
                                           RowFrag (&wf)[WIDE_SLOTS][NT], RowFrag (&af)[WIDE_SLOTS],
                                           ActChunk<WPG>* act, f32x4 (&acc)[NT][MT], const uint8_t* ac,
@@ -379,14 +431,14 @@ __device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c
     if constexpr (LOADS) {
         load_full(ac, as, cl, af[dn]);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], cl, wf[dn][t]);
+        for (int t = 0; t < WIDE_NT; ++t) load_w<PK>(wc[t], ws[t], cl, false, 0, 0, wf[dn][t]);
     }
     __builtin_amdgcn_sched_barrier(0);  // issue them before waiting for chunk c
     __syncthreads();                    // chunk c converted; every wave is done with the other buffer
     const bool live = c < c_fhi;
 #pragma unroll
     for (int t = 0; t < WIDE_NT; ++t) wf[d][t].s = live ? wf[d][t].s : 0u;
-    compute_lds<MT, NT, WPG>(wf[d], act[i & 1], lane, acc);
+    compute_lds<MT, NT, WPG, PK>(wf[d], act[i & 1], lane, acc);
     stage_act<WPG>(act[(i + 1) & 1], af[(d + 1) % WIDE_SLOTS], u, lane);
     // keep the next chunk's dequantization out of this one (it would wait for its loads)
     __builtin_amdgcn_sched_barrier(0);
@@ -394,7 +446,7 @@ __device__ __forceinline__ void wide_step(int d, int64_t i, int64_t c, int64_t c
 
 // A workgroup is two K-groups of WPG waves, each wave NT weight tiles of 16 rows: WPG * 16 * NT
 // weight rows.
-template <int MT, int NT, int WPG>
+template <int MT, int NT, int WPG, bool PK>
 __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
     const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
     const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
@@ -419,11 +471,7 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
     const uint8_t* wc[WIDE_NT];
     const uint8_t* ws[WIDE_NT];
 #pragma unroll
-    for (int t = 0; t < WIDE_NT; ++t) {
-        const int64_t n = std::min<int64_t>(n0 + 16 * t + rl, N - 1);
-        wc[t] = w_codes + n * ldw_c + 16 * q;
-        ws[t] = w_scales + n * ldw_s + 4 * q;
-    }
+    for (int t = 0; t < WIDE_NT; ++t) w_pointers<PK>(w_codes, ldw_c, w_scales, ldw_s, n0 + 16 * t, N, K, lane, wc[t], ws[t]);
     const int64_t arow = std::min<int64_t>(16 * u + rl, M - 1);
     const uint8_t* ac = a_codes + arow * lda_c + 16 * q;
     const uint8_t* as = a_scales + arow * lda_s + 4 * q;
@@ -448,23 +496,23 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
         // step by step, in the loop's order, so that the loop's waits count the same loads on entry
         load_full(ac, as, clamped(0), af[0]);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], clamped(0), wf[0][t]);
+        for (int t = 0; t < WIDE_NT; ++t) load_w<PK>(wc[t], ws[t], clamped(0), false, 0, 0, wf[0][t]);
         load_full(ac, as, clamped(1), af[1]);
 #pragma unroll
-        for (int t = 0; t < WIDE_NT; ++t) load_full(wc[t], ws[t], clamped(1), wf[1][t]);
+        for (int t = 0; t < WIDE_NT; ++t) load_w<PK>(wc[t], ws[t], clamped(1), false, 0, 0, wf[1][t]);
         stage_act<WPG>(act[0], af[0], u, lane);
         int64_t i0 = 0;
         for (; i0 + WIDE_SLOTS <= steps; i0 += WIDE_SLOTS) {
 #pragma unroll
             for (int d = 0; d < WIDE_SLOTS; ++d)
-                wide_step<MT, NT, WPG, true>(d, i0 + d, chunk(i0 + d), c_fhi, clamped(i0 + d + 2), wf, af, act,
+                wide_step<MT, NT, WPG, PK, true>(d, i0 + d, chunk(i0 + d), c_fhi, clamped(i0 + d + 2), wf, af, act,
                                              acc, ac, as, wc, ws, u, lane);
         }
         // the last one or two steps: their chunks are already loaded (slots 0 and 1)
         if (i0 < steps)
-            wide_step<MT, NT, WPG, false>(0, i0, chunk(i0), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
+            wide_step<MT, NT, WPG, PK, false>(0, i0, chunk(i0), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u, lane);
         if (i0 + 1 < steps)
-            wide_step<MT, NT, WPG, false>(1, i0 + 1, chunk(i0 + 1), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u,
+            wide_step<MT, NT, WPG, PK, false>(1, i0 + 1, chunk(i0 + 1), c_fhi, 0, wf, af, act, acc, ac, as, wc, ws, u,
                                           lane);
     }
     if (c_fhi < c_hi) {
@@ -475,11 +523,11 @@ __global__ __launch_bounds__(128 * WPG) void gemm_wide_kernel(
             RowFrag taf;
             load_tail(ac, as, c_fhi, q, K, taf);
 #pragma unroll
-            for (int t = 0; t < WIDE_NT; ++t) load_tail(wc[t], ws[t], c_fhi, q, K, twf[t]);
+            for (int t = 0; t < WIDE_NT; ++t) load_w<PK>(wc[t], ws[t], c_fhi, true, q, K, twf[t]);
             stage_act<WPG>(act[0], taf, u, lane);
         }
         __syncthreads();
-        if (kg == 0) compute_lds<MT, NT, WPG>(twf, act[0], lane, acc);
+        if (kg == 0) compute_lds<MT, NT, WPG, PK>(twf, act[0], lane, acc);
     }
 
     // K-group 0 + K-group 1, through LDS. acc[t][uu] of lane (g, r) holds y[n0 + 16t + 4g + e][16uu + r].
@@ -581,6 +629,48 @@ void launch_reduce(const float* partial, int64_t M, int64_t N, const SegParams& 
 
 }  // namespace
 
+// The decode weight layout from row-major NVFP4 weights: one thread per (tile, chunk, lane) writes the
+// lane's two 16-byte code pieces and its scale dword (zeros past N and K).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ w_codes, int64_t ldw_c,
+                                                           const uint8_t* __restrict__ w_scales, int64_t ldw_s,
+                                                           int64_t N, int64_t K, int64_t C, int64_t units,
+                                                           uint8_t* __restrict__ codes_out,
+                                                           uint8_t* __restrict__ scales_out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units) return;
+    const int lane = (int)(i & 63);
+    const int64_t tc = i >> 6, t = tc / C, c = tc - t * C;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n = 16 * t + r;
+    u32x4 piece[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    uint32_t sv = 0;
+    if (n < N) {
+        const uint8_t* row = w_codes + n * ldw_c;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t off = c * (CHUNK / 2) + 64 * h + 16 * g;
+            const int64_t v = K / 2 - off;  // K is a multiple of 16: a piece is full, half or empty
+            if (v >= 16) {
+                piece[h] = *reinterpret_cast<const u32x4*>(row + off);
+            } else if (v >= 8) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(row + off);
+                piece[h] = u32x4{lo[0], lo[1], 0u, 0u};
+            }
+        }
+        const uint8_t* srow = w_scales + n * ldw_s;
+        const int blk[4] = {2 * g, 2 * g + 1, 8 + 2 * g, 9 + 2 * g};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t b = c * (CHUNK / 16) + blk[e];
+            if (b < K / 16) sv |= (uint32_t)srow[b] << (8 * e);
+        }
+    }
+    uint8_t* dst = codes_out + tc * PK_CODES + 16 * lane;
+    *reinterpret_cast<u32x4*>(dst) = piece[0];
+    *reinterpret_cast<u32x4*>(dst + 1024) = piece[1];
+    *reinterpret_cast<uint32_t*>(scales_out + tc * PK_SCALES + 4 * lane) = sv;
+}
+
 // K split of the wide decode kernel, from K alone (so output bits do not depend on N): at least 11
 // chunks of 256 per split, at most 8 splits, an even number of chunks per split (the two K-groups
 // take alternate chunks), so the last split may be shorter. A workgroup holds a whole CU (8 waves of
@@ -639,10 +729,31 @@ size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return splits > 1 ? (size_t)splits * (size_t)N * WIDE_MP * sizeof(float) : 0;
 }
 
+size_t packed_weight_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return 0;
+    const int64_t T = (N + 15) / 16, C = (K + CHUNK - 1) / CHUNK;
+    return (size_t)T * (size_t)C * (PK_CODES + PK_SCALES);
+}
+
+const uint8_t* packed_scales(const uint8_t* packed, int64_t N, int64_t K) {
+    const int64_t T = (N + 15) / 16, C = (K + CHUNK - 1) / CHUNK;
+    return packed + T * C * PK_CODES;
+}
+
+hipError_t launch_pack_weights(const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                               int64_t N, int64_t K, uint8_t* packed, hipStream_t stream) {
+    if (N <= 0 || K <= 0) return hipSuccess;
+    const int64_t T = (N + 15) / 16, C = (K + CHUNK - 1) / CHUNK, units = T * C * 64;
+    if ((units + 255) / 256 > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((uint32_t)((units + 255) / 256)), dim3(256), 0, stream, w_codes,
+                       ldw_c, w_scales, ldw_s, N, K, C, units, packed, packed + T * C * PK_CODES);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                             const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                             int64_t M, int64_t N, int64_t K, const SegParams& sp, void* workspace,
-                            hipStream_t stream) {
+                            bool packed, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const WideSplit ks = wide_split(K);
     if (M <= SKINNY_NARROW_M || M > SKINNY_MAX_M || (ks.splits > 1 && !workspace)) return hipErrorInvalidValue;
@@ -654,12 +765,21 @@ hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t
     using wide_fn = void (*)(const uint8_t*, int64_t, const uint8_t*, int64_t, const uint8_t*, int64_t,
                              const uint8_t*, int64_t, int64_t, int64_t, int64_t, int64_t, float*, const SegParams);
     wide_fn fn;
-    if (sh.wpg == 4 && sh.nt == 2)
-        fn = mt == 3 ? gemm_wide_kernel<3, 2, 4> : gemm_wide_kernel<4, 2, 4>;
-    else if (sh.wpg == 5)
-        fn = mt == 3 ? gemm_wide_kernel<3, 1, 5> : gemm_wide_kernel<4, 1, 5>;
-    else
-        fn = mt == 3 ? gemm_wide_kernel<3, 1, 4> : gemm_wide_kernel<4, 1, 4>;
+    if (packed) {
+        if (sh.wpg == 4 && sh.nt == 2)
+            fn = mt == 3 ? gemm_wide_kernel<3, 2, 4, true> : gemm_wide_kernel<4, 2, 4, true>;
+        else if (sh.wpg == 5)
+            fn = mt == 3 ? gemm_wide_kernel<3, 1, 5, true> : gemm_wide_kernel<4, 1, 5, true>;
+        else
+            fn = mt == 3 ? gemm_wide_kernel<3, 1, 4, true> : gemm_wide_kernel<4, 1, 4, true>;
+    } else {
+        if (sh.wpg == 4 && sh.nt == 2)
+            fn = mt == 3 ? gemm_wide_kernel<3, 2, 4, false> : gemm_wide_kernel<4, 2, 4, false>;
+        else if (sh.wpg == 5)
+            fn = mt == 3 ? gemm_wide_kernel<3, 1, 5, false> : gemm_wide_kernel<4, 1, 5, false>;
+        else
+            fn = mt == 3 ? gemm_wide_kernel<3, 1, 4, false> : gemm_wide_kernel<4, 1, 4, false>;
+    }
     hipLaunchKernelGGL(fn, dim3((uint32_t)(groups * ks.splits)), dim3(128 * sh.wpg), 0, stream, a_codes, lda_c,
                        a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, ks.per, partial, sp);
     if (ks.splits > 1) {
@@ -674,7 +794,8 @@ hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
-                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream) {
+                              int64_t M, int64_t N, int64_t K, const SegParams& sp, bool packed,
+                              hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M > SKINNY_MAX_M) return hipErrorInvalidValue;
     const int mt = (int)((M + 15) / 16);
@@ -683,10 +804,14 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8
     // Measured on the MLP and GDN projection shapes (N = 5120 .. 17408, K = 5120 .. 17408); N only
     // decides how columns are grouped, never the order of any sum.
     const int nt = M <= 4 ? 1 : 2;
-    const skinny_fn fn = mt == 1   ? pick_nt<1>(nt)
-                         : mt == 2 ? pick_nt<2>(nt)
-                         : mt == 3 ? pick_nt<3>(nt)
-                                   : pick_nt<4>(nt);
+    const skinny_fn fn = packed ? (mt == 1   ? pick_nt<1, true>(nt)
+                                   : mt == 2 ? pick_nt<2, true>(nt)
+                                   : mt == 3 ? pick_nt<3, true>(nt)
+                                             : pick_nt<4, true>(nt))
+                                : (mt == 1   ? pick_nt<1, false>(nt)
+                                   : mt == 2 ? pick_nt<2, false>(nt)
+                                   : mt == 3 ? pick_nt<3, false>(nt)
+                                             : pick_nt<4, false>(nt));
     const int kw = skinny_waves(K);
     const size_t lds = (size_t)kw * nt * mt * 256 * sizeof(float);
     const int64_t blocks = (N + 16 * nt - 1) / (16 * nt);

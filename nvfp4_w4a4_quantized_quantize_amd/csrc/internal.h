@@ -49,14 +49,23 @@ constexpr int64_t SKINNY_MAX_M = 64;
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                              const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+// The decode launchers take row-major weights (w_codes, ldw_c, w_scales, ldw_s), or, with packed,
+// the decode weight layout: w_codes = its codes (the layout's base), w_scales = packed_scales(), the
+// strides unused.
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                               const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
-                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);
+                              int64_t M, int64_t N, int64_t K, const SegParams& sp, bool packed,
+                              hipStream_t stream);
 // SKINNY_NARROW_M < M <= SKINNY_MAX_M; workspace holds gemm_wide_workspace_bytes(M, N, K) bytes.
 hipError_t launch_gemm_wide(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                             const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                             int64_t M, int64_t N, int64_t K, const SegParams& sp, void* workspace,
-                            hipStream_t stream);
+                            bool packed, hipStream_t stream);
+// The decode weight layout (nvfp4_pack_weights): its size, where its scales start, and the repack.
+size_t packed_weight_bytes(int64_t N, int64_t K);
+const uint8_t* packed_scales(const uint8_t* packed, int64_t N, int64_t K);
+hipError_t launch_pack_weights(const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
+                               int64_t N, int64_t K, uint8_t* packed, hipStream_t stream);
 // Bytes of FP32 partial sums the wide variant keeps (0 outside its range of M).
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

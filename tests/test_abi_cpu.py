@@ -275,3 +275,52 @@ def test_gemm_noalloc_rejects_before_any_launch(L):
     assert "scratch" in nv.last_error()
     assert call(8, 64, 40, 32, 16) == 2
     assert call(0, 64, 64, 32, 16) == 0
+
+
+def test_packed_weight_bytes(L):
+    """The decode layout holds 2304 bytes per 16-row tile and 256-element chunk."""
+    W = L.nvfp4_packed_weight_bytes
+    assert W(16, 256) == 2304 and W(17, 256) == W(16, 272) == 2 * 2304
+    assert W(17408, 5120) == 1088 * 20 * 2304 and W(5120, 17408) == 320 * 68 * 2304
+    assert W(0, 256) == W(16, 0) == W(16, 24) == W(-1, 16) == 0
+
+
+def pack(L, w_codes=A16, ldw_c=32, w_scales=A16, ldw_s=16, N=20, K=64, packed=A16):
+    return L.nvfp4_pack_weights(w_codes, ldw_c, w_scales, ldw_s, N, K, packed, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_codes=None), 1), (dict(w_scales=None), 1), (dict(packed=None), 1),
+    (dict(K=24), 2), (dict(N=-1), 2), (dict(ldw_c=16), 2),
+    (dict(packed=A16 + 4), 3), (dict(w_codes=A16 + 8), 3), (dict(ldw_s=20), 3),
+])
+def test_pack_weights_rejects(L, kw, status):
+    assert pack(L, **kw) == status
+    assert nv.last_error() != ""
+
+
+def test_pack_weights_empty_is_a_no_op(L):
+    assert pack(L, N=0, packed=None) == 0
+    assert pack(L, K=0, packed=None) == 0
+
+
+def gp(L, M=8, N=64, K=64, packed=A16, segs=None, g_a=1.0):
+    if segs is None:
+        segs = [(0, N, 0, 0, A16, N, None, None)]
+    gw = (ctypes.c_float * len(segs))(*([1.0] * len(segs)))
+    return L.nvfp4_gemm_packed(A16, 32, A16, 16, g_a, packed, M, N, K, seg_array(segs), gw, len(segs), None, 0,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=65), 2), (dict(M=4096), 2), (dict(K=24), 2), (dict(packed=None), 1), (dict(packed=A16 + 4), 3),
+    (dict(segs=[(0, 32, 0, 0, A16, 32, None, None)]), 4), (dict(g_a=0.0), 5),
+])
+def test_gemm_packed_rejects(L, kw, status):
+    assert gp(L, **kw) == status
+    assert nv.last_error() != ""
+
+
+def test_gemm_packed_empty_is_a_no_op(L):
+    assert gp(L, M=0) == 0
+    assert gp(L, N=0, segs=[]) != 0  # an empty segment table is rejected as for nvfp4_gemm
