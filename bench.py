@@ -14,7 +14,8 @@ Prints one JSON line. `value` is the step's throughput in GEMM TFLOP/s (2 M N K 
 activation (1 GB of input per round, more than the last-level cache); `cpu_baseline` the CPU oracle on
 a bounded sample of the same step, extrapolated linearly in M, on all host threads and on one;
 `other_configs` the GEMMs of the other workloads (prefill projection, fused MLP gate+up, the six
-decode GEMMs), each over rotating weight copies, with its own roofline.
+decode GEMMs, and the four decode GEMMs with M > 1 again with the weights in the decode layout,
+`*_packed`), each over rotating weight copies, with its own roofline.
 """
 from __future__ import annotations
 
@@ -73,8 +74,9 @@ def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
 class Step:
     """Device buffers and the launches of one step of the fused GDN input projection."""
 
-    def __init__(self, case: wl.GemmCase, seed: int = 0, copies: int = 1):
+    def __init__(self, case: wl.GemmCase, seed: int = 0, copies: int = 1, packed: bool = False):
         self.case = case
+        self.packed = packed
         M, K, N = case.M, case.K, case.N
         dev = torch.device("cuda")
         t0 = time.time()
@@ -98,6 +100,8 @@ class Step:
         self.w_copies = [(self.w_codes, self.w_scales)]
         for _ in range(copies - 1):
             self.w_copies.append((self.w_codes.clone(), self.w_scales.clone()))
+        # the decode weight layout of each copy, repacked once (offline) for gemm_packed
+        self.w_packed = [nv.pack_weights(c, sc) for c, sc in self.w_copies] if packed else []
         self.calls = 0
         # static activation calibration
         self.g_a = float(nv.global_scale(self.x).item())
@@ -121,9 +125,14 @@ class Step:
         nv.quantize(self.x, self.g_a, self.a_codes, self.a_scales)
 
     def gemm(self):
-        wc, ws = self.w_copies[self.calls % len(self.w_copies)]
+        i = self.calls % len(self.w_copies)
         self.calls += 1
-        nv.gemm(self.a_codes, self.a_scales, self.g_a, wc, ws, self.segments, workspace=self.workspace)
+        if self.packed:
+            nv.gemm_packed(self.a_codes, self.a_scales, self.g_a, self.w_packed[i], self.case.N, self.segments,
+                           workspace=self.workspace)
+        else:
+            wc, ws = self.w_copies[i]
+            nv.gemm(self.a_codes, self.a_scales, self.g_a, wc, ws, self.segments, workspace=self.workspace)
 
 
 def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
@@ -197,13 +206,16 @@ def time_quantizer_rotating(step: Step, copies: int = 3, reps: int = 10) -> dict
     return {"ms": ms, "rotation_bytes": in_bytes, "copies": copies, "launches": reps * copies}
 
 
-def decode_kernel_name(M: int, K: int) -> str:
-    """The kernel the library runs for M <= 32 activation rows: the weight-streaming GEMV for one row
-    (K from 16 to 32768), else the skinny kernel."""
+def decode_kernel_name(M: int, K: int, packed: bool = False) -> str:
+    """The kernel the library runs for M <= 32 activation rows: with row-major weights the
+    weight-streaming GEMV for one row (K from 16 to 32768), else (and always with packed weights) the
+    skinny kernel."""
+    if packed:
+        return "gemm_skinny_kernel (packed weights)"
     return "gemm_gemv_kernel" if M == 1 and 16 <= K <= 32768 else "gemm_skinny_kernel"
 
 
-def gemm_roofline(case: wl.GemmCase, ms: float) -> dict:
+def gemm_roofline(case: wl.GemmCase, ms: float, packed: bool = False) -> dict:
     """TFLOP/s, GB/s and the roofline the GEMM of `case` runs against: the dense FP16 MFMA peak above
     the ridge point (peak FLOP/s per HBM byte/s), HBM bandwidth below it."""
     M, N, K = case.M, case.N, case.K
@@ -221,9 +233,9 @@ def gemm_roofline(case: wl.GemmCase, ms: float) -> dict:
         kernel = "gemm_kernel"
     elif M > 32:
         kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if nv.lib().nvfp4_gemm_workspace_bytes(M, N, K)
-                                       else "")
+                                       else "") + (" (packed weights)" if packed else "")
     else:
-        kernel = decode_kernel_name(M, K)
+        kernel = decode_kernel_name(M, K, packed)
     roof.update({"kernel": kernel, "avg_ms": ms, "algorithmic_flop": flops, "algorithmic_bytes": nbytes})
     return {"ms": ms, "tflops": tflops, "gbps": gbps, "roofline": roof}
 
@@ -238,6 +250,8 @@ def weight_copies(case: wl.GemmCase) -> int:
 
 
 OTHER_CONFIGS = ("C2", "C4", "C3_up_1", "C3_up_16", "C3_up_64", "C3_down_1", "C3_down_16", "C3_down_64")
+# decode GEMMs also timed with the weights in the decode layout (nvfp4_gemm_packed)
+PACKED_CONFIGS = ("C3_up_16", "C3_up_64", "C3_down_16", "C3_down_64")
 
 
 def bench_other_configs(reps: int) -> dict:
@@ -245,17 +259,17 @@ def bench_other_configs(reps: int) -> dict:
     events on the library's stream, after a few untimed calls): prefill projection 4096x5120x5120,
     fused MLP gate+up 8192x34816x5120, and the six decode GEMMs (HBM-bound weight streaming)."""
     res = {}
-    for key in OTHER_CONFIGS:
+    for key, packed in [(k, False) for k in OTHER_CONFIGS] + [(k, True) for k in PACKED_CONFIGS]:
         case = wl.ALL[key]
-        step = Step(case, copies=weight_copies(case))
+        step = Step(case, copies=weight_copies(case), packed=packed)
         step.quantize()
         n = max(reps, 4 * len(step.w_copies))
         _settle(lambda i: step.gemm(), 0.1)
         ms = _time_loop(lambda i: step.gemm(), n)
-        r = gemm_roofline(case, ms)
-        r.update({"workload": case.name, "M": case.M, "N": case.N, "K": case.K, "weight_copies": len(step.w_copies),
-                  "launches": n})
-        res[key] = r
+        r = gemm_roofline(case, ms, packed)
+        r.update({"workload": case.name + ("_packed" if packed else ""), "M": case.M, "N": case.N, "K": case.K,
+                  "weight_copies": len(step.w_copies), "launches": n})
+        res[key + ("_packed" if packed else "")] = r
         log(f"[gpu] {case.name}: {ms * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s, {r['gbps']:.0f} GB/s "
             f"({r['roofline']['bound']} {100 * r['roofline']['frac']:.1f}%)")
         del step
@@ -625,6 +639,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C5", choices=sorted(wl.ALL) + list(COMPANIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--packed", action="store_true",
+                    help="decode GEMM workloads (M <= 64): weights in the decode layout (nvfp4_gemm_packed)")
     ap.add_argument("--cpu-rows-quant", type=int, default=32768)
     ap.add_argument("--cpu-rows-gemm", type=int, default=4096)
     ap.add_argument("--flush-mb", type=int, default=-1,
@@ -655,7 +671,10 @@ def main() -> int:
     # a step whose working set fits the 256 MB last-level cache would be served from it: such steps
     # rotate through copies of the weights, 1 GiB in all
     copies = weight_copies(case)
-    step = Step(case, copies=copies)
+    if args.packed and case.M > 64:
+        print("--packed serves the decode GEMMs (M <= 64)", file=sys.stderr)
+        return 2
+    step = Step(case, copies=copies, packed=args.packed)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -693,9 +712,10 @@ def main() -> int:
     if M > 64:
         kernel = "gemm_kernel"
     elif M > 32:  # the reduce kernel runs only when K is split over workgroups (the workspace holds the parts)
-        kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if step.workspace is not None else "")
+        kernel = "gemm_wide_kernel" + (" + gemm_wide_reduce_kernel" if step.workspace is not None else "") + \
+            (" (packed weights)" if args.packed else "")
     else:
-        kernel = decode_kernel_name(M, K)
+        kernel = decode_kernel_name(M, K, args.packed)
     tr = measured_traffic(kernel, case.name)
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,
