@@ -33,6 +33,11 @@
 //  * Tiles are ordered for the 8 XCDs (each with its own L2): workgroup b runs on XCD b % 8, so each
 //    XCD gets a contiguous range of full-width tiles, walked in groups of 8 M-tiles so that
 //    concurrently running tiles share A and W panels in L2; the partial column's tiles run last.
+//  * When the full tiles' last round would leave CUs idle (C2's 320 tiles on 256 CUs: a second round
+//    a quarter full), the trailing tile columns that make up that round run as 128- or 64-column
+//    tiles instead, as many as fit one round. A narrow tile is computed exactly like the partial
+//    column's (waves stacked along M), and its weight buffer resource covers only its own rows, so the
+//    loads of the other rows fetch nothing. Every output's sum runs in the same order either way.
 //  * Epilogue: the W fragment is the MFMA's first operand, so each lane holds runs of 4 consecutive
 //    output columns of one row. Accumulators are staged per wave through LDS (one 16-byte write per
 //    run), 64 columns at a time; column ranges of a plain segment are scaled and written with 16-byte
@@ -388,7 +393,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Se
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const uint8_t* __restrict__ a_codes, int64_t lda_c, const uint8_t* __restrict__ a_scales, int64_t lda_s,
     const uint8_t* __restrict__ w_codes, int64_t ldw_c, const uint8_t* __restrict__ w_scales, int64_t ldw_s,
-    int64_t M, int64_t N, int64_t K, int32_t tiles_m, const SegParams sp) {
+    int64_t M, int64_t N, int64_t K, const TileMap tmap, const SegParams sp) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -398,35 +403,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int lh = lane >> 5;  // lane half: which 8-element K group of an MFMA step
 
     // ---- tile order ---------------------------------------------------------------------------------
-    // Tiles of the full-width tile columns come first: contiguous per XCD, grouped by GROUP_M M-tiles
-    // inside it. The tiles of a partial last column (fewer than BN columns of N) come last, one per
-    // M-tile, so that the cheaper ones fill the final, partly occupied round of workgroups.
-    int tm, tn;
+    // Tiles of the first tmap.tn_wide full-width tile columns come first: contiguous per XCD, grouped
+    // by GROUP_M M-tiles inside it. Then the narrow tiles, one per M-tile and narrow column: the next
+    // tmap.split_cols tile columns cut into tmap.pieces columns of BN / pieces, then the partial last
+    // column (fewer than BN columns of N), so that the cheaper tiles fill the final rounds.
+    const int tiles_m = tmap.tiles_m;
+    int tm;
+    int64_t n0, n_end;  // the tile's columns [n0, n_end)
     {
-        const int tn_full = (int)(N / BN);
-        const int T = tiles_m * tn_full;
+        const int T = tiles_m * tmap.tn_wide;
         const int bid = blockIdx.x;
         if (bid >= T) {
-            tm = bid - T;
-            tn = tn_full;
+            const int j = bid - T, nc = j / tiles_m, narrow = tmap.split_cols * tmap.pieces;
+            tm = j - nc * tiles_m;
+            if (nc < narrow) {
+                const int width = BN / tmap.pieces;
+                n0 = (int64_t)(tmap.tn_wide + nc / tmap.pieces) * BN + (int64_t)(nc % tmap.pieces) * width;
+                n_end = n0 + width;
+            } else {
+                n0 = (int64_t)(tmap.tn_wide + tmap.split_cols) * BN;
+                n_end = N;
+            }
         } else {
             const int xcd = bid & 7, local = bid >> 3;
             const int q = T >> 3, rem = T & 7;
             const int vt = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
-            const int per_group = GROUP_M * tn_full;
+            const int per_group = GROUP_M * tmap.tn_wide;
             const int g = vt / per_group, in_g = vt - g * per_group;
             const int first_m = g * GROUP_M;
             const int gm = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
             tm = first_m + in_g % gm;
-            tn = in_g / gm;
+            n0 = (int64_t)(in_g / gm) * BN;
+            n_end = n0 + BN;
         }
     }
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)tm * BM;
 
     // Wave layout: 2 x 2 waves of 128 x 128 in a tile with more than 128 columns; with at most 128
     // columns, 4 x 1 waves of 64 rows x 128 columns (so that all four waves have work).
-    const int64_t n_tile = N - n0 < BN ? N - n0 : BN;
-    const bool stacked = n_tile <= 128;
+    const bool stacked = n_end - n0 <= 128;
     const int wm = stacked ? wave : wave >> 1, wn = stacked ? 0 : wave & 1;
     const int64_t row0 = m0 + (stacked ? 64 : 128) * wm;  // first output row of this wave
     const int64_t col0 = n0 + 128 * wn;                    // first output column of this wave
@@ -455,10 +470,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // kc + 1's scales and first codes, and step 15 dequantizes its first step, so the MFMA stream
     // runs on across the chunk boundary.
     const int64_t nk = (K + BK - 1) / BK;
-    const int64_t n_wave = N - col0;  // columns of this wave that exist (> 0 in either layout)
+    const int64_t n_wave = n_end - col0;  // columns of this wave in the tile (> 0 in either layout)
     const uint32_t rsub = lane >> 3;
-    const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, N, ldw_c),
-                    tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, N, ldw_s),
+    const Loader ld{tile_rsrc(a_codes, m0, M, lda_c), tile_rsrc(w_codes, n0, n_end, ldw_c),
+                    tile_rsrc(a_scales, m0, M, lda_s), tile_rsrc(w_scales, n0, n_end, ldw_s),
                     (uint32_t)lda_c, (uint32_t)ldw_c, (uint32_t)lda_s, (uint32_t)ldw_s,
                     rsub * (uint32_t)lda_c, rsub * (uint32_t)ldw_c, (uint32_t)lane * (uint32_t)lda_s,
                     (uint32_t)lane * (uint32_t)ldw_s, 16u * ((lane & 7) ^ rsub), wave};
@@ -494,13 +509,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 
 }  // namespace
 
+TileMap tile_map(int64_t M, int64_t N, int cus) {
+    TileMap t{(int32_t)((M + BM - 1) / BM), (int32_t)(N / BN), 0, 1};
+    const int64_t full = (int64_t)t.tiles_m * t.tn_wide, partial = N % BN ? t.tiles_m : 0;
+    const int64_t rest = full % cus;  // full tiles of the last, partly occupied round
+    if (rest == 0) return t;
+    const int64_t cols = std::min<int64_t>(t.tn_wide, (rest + t.tiles_m - 1) / t.tiles_m);
+    const int64_t fit = (cus - partial) / (cols * t.tiles_m);  // pieces per column that still fit one round
+    if (fit < 2) return t;
+    t.split_cols = (int32_t)cols;
+    t.pieces = fit >= 4 ? 4 : 2;
+    t.tn_wide -= t.split_cols;
+    return t;
+}
+
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                              const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(tiles_m * tiles_n)), dim3(NTHREADS), 0, stream, a_codes,
-                       lda_c, a_scales, lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, (int32_t)tiles_m, sp);
+    const TileMap t = tile_map(M, N, device_cus());
+    const int64_t blocks = (int64_t)t.tiles_m * (t.tn_wide + t.split_cols * t.pieces + (N % BN ? 1 : 0));
+    hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)blocks), dim3(NTHREADS), 0, stream, a_codes, lda_c, a_scales,
+                       lda_s, w_codes, ldw_c, w_scales, ldw_s, M, N, K, t, sp);
     return hipGetLastError();
 }
 

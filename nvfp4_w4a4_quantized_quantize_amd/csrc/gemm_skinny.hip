@@ -696,9 +696,7 @@ struct WideShape {
     int rows, wpg, nt;
 };
 
-// CUs of the current device (a host query of the device's properties; it neither allocates nor
-// synchronizes).
-static int device_cus() {
+int device_cus() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)

@@ -46,6 +46,18 @@ hipError_t launch_gemm_gemv(const uint8_t* a_codes, int64_t lda_c, const uint8_t
 constexpr int64_t SKINNY_NARROW_M = 32;
 constexpr int64_t SKINNY_MAX_M = 64;
 
+// CUs of the current device (a host query of its properties; it neither allocates nor synchronizes).
+int device_cus();
+
+// Grid of the tiled kernel: tiles_m tiles of 256 rows; the first tn_wide tile columns of 256 run as
+// full tiles, the next split_cols as pieces columns of 256 / pieces (1, 2 or 4) each, then the
+// partial last column if N is not a multiple of 256. Columns are split only when the full tiles'
+// last round would leave CUs idle and the pieces of the split columns fit in one round.
+struct TileMap {
+    int32_t tiles_m, tn_wide, split_cols, pieces;
+};
+TileMap tile_map(int64_t M, int64_t N, int cus);
+
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_scales, int64_t lda_s,
                              const uint8_t* w_codes, int64_t ldw_c, const uint8_t* w_scales, int64_t ldw_s,
                              int64_t M, int64_t N, int64_t K, const SegParams& sp, hipStream_t stream);

@@ -143,6 +143,67 @@ def test_tile_layouts_and_epilogue_kernels(name):
             check_bf16(out, ys, Ts, f"{name} segment {s}")
 
 
+def _check_outputs(outs, spec, y, T, bounds, tag):
+    for s, out in enumerate(outs):
+        lo, hi = bounds[s], bounds[s + 1]
+        ys, Ts = y[:, lo:hi], T[:, lo:hi]
+        n, _, epi, dt, al, db = spec[s]
+        if epi == "sigmoid":
+            check_sigmoid(host(out), ys, Ts, oracle.sigmoid(ys))
+        elif epi == "gdn_decay":
+            check_decay(host(out), ys, Ts, oracle.gdn_decay(ys, al, db), al, db)
+        elif dt == torch.float32:
+            check_fp32(host(out), ys, Ts, f"{tag} segment {s}")
+        else:
+            check_bf16(out, ys, Ts, f"{tag} segment {s}")
+
+
+def _spec_from(layout, rng):
+    spec = []
+    for n, gw, epi, dt in layout:
+        al = db = None
+        if epi == "gdn_decay":
+            al = (rng.standard_normal(n) * 0.5).astype(np.float32)
+            db = (rng.standard_normal(n) * 0.5).astype(np.float32)
+        spec.append((n, gw, epi, dt, al, db))
+    return spec
+
+
+def test_full_tiles_with_gates_mid_n():
+    """Gate and plain segments inside full 256 x 256 tiles (2 x 2 waves). 9 M-tiles x 15 full tile
+    columns are 135 tiles, too many for their pieces to fit one round of 256 CUs, so no column is
+    split; the 64-column tail holds a gate segment."""
+    rng = np.random.default_rng(2100)
+    M, K = 2100, 528
+    layout = [(1024, 1.0, "none", torch.bfloat16), (64, 0.6, "sigmoid", torch.float32),
+              (1000, 1.1, "none", torch.bfloat16), (88, 0.8, "gdn_decay", torch.float32),
+              (1664, 1.2, "none", torch.float32), (64, 0.9, "sigmoid", torch.float32)]
+    N = sum(n for n, *_ in layout)
+    a, w = random_nvfp4(rng, M, K, 0x20, 0x50), random_nvfp4(rng, N, K, 0x20, 0x50)
+    spec = _spec_from(layout, rng)
+    g_a = np.float32(2.0 ** -6)
+    outs = run_gemm(a, w, g_a, spec, K)
+    (y, T), bounds = oracle_y(a, w, g_a, spec, np.arange(M))
+    _check_outputs(outs, spec, y, T, bounds, "full tiles")
+
+
+# Shapes whose full tiles leave most CUs idle in their last round (on 256 CUs): trailing tile columns
+# run as 128-column (1000 x 6450, 2048 x 2148, 4096 x 5184) or 64-column (512 x 1000) pieces, next to
+# the partial last column; segment boundaries and gates fall inside and across the pieces.
+@pytest.mark.parametrize("M,N,K", [(1000, 6450, 272), (2048, 2148, 528), (512, 1000, 1040), (4096, 5184, 256)])
+def test_split_tail_tile_columns(M, N, K):
+    rng = np.random.default_rng(M + 7 * N + K)
+    n1 = (N // 3) | 1
+    layout = [(n1, 0.75, "none", torch.bfloat16), (40, 1.3, "sigmoid", torch.float32),
+              (72, 0.9, "gdn_decay", torch.float32), (N - n1 - 112, 1.5, "none", torch.float32)]
+    a, w = random_nvfp4(rng, M, K, 0x20, 0x58), random_nvfp4(rng, N, K, 0x20, 0x58)
+    spec = _spec_from(layout, rng)
+    g_a = np.float32(0.03)
+    outs = run_gemm(a, w, g_a, spec, K)
+    (y, T), bounds = oracle_y(a, w, g_a, spec, np.arange(M))
+    _check_outputs(outs, spec, y, T, bounds, f"M={M} N={N} K={K}")
+
+
 def test_fused_equals_unfused_bitwise_and_repeatable():
     rng = np.random.default_rng(7)
     M, K = 200, 640
