@@ -798,10 +798,12 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, int64_t lda_c, const uint8
     if (M > SKINNY_MAX_M) return hipErrorInvalidValue;
     const int mt = (int)((M + 15) / 16);
     // Two weight tiles per wave share each activation fragment; with one or a few activation rows
-    // those loads are cheap and one tile per wave (twice the workgroups) streams the weights faster.
-    // Measured on the MLP and GDN projection shapes (N = 5120 .. 17408, K = 5120 .. 17408); N only
-    // decides how columns are grouped, never the order of any sum.
-    const int nt = M <= 4 ? 1 : 2;
+    // those loads are cheap and one tile per wave (twice the workgroups) streams the weights faster,
+    // and up to 16 rows so does a grid of at least 4 one-tile workgroups per CU (MLP up 17408 x 5120:
+    // 18.6 -> 15.7 us at M = 8, 20.0 -> 18.5 at M = 16; packed 15.4 -> 14.3, 16.4 -> 15.5). Measured
+    // on the MLP and GDN projection shapes (N = 5120 .. 17408, K = 5120 .. 17408); N only decides how
+    // columns are grouped, never the order of any sum.
+    const int nt = (M <= 4 || (M <= 16 && (N + 15) / 16 >= 4 * (int64_t)device_cus())) ? 1 : 2;
     const skinny_fn fn = packed ? (mt == 1   ? pick_nt<1, true>(nt)
                                    : mt == 2 ? pick_nt<2, true>(nt)
                                    : mt == 3 ? pick_nt<3, true>(nt)

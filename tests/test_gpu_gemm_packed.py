@@ -68,7 +68,7 @@ def both(a, w, g_a, g_w, dtype=torch.float32):
 
 
 @pytest.mark.parametrize("M", [2, 5, 16, 17, 32, 33, 48, 64])
-@pytest.mark.parametrize("N,K", [(17, 48), (100, 272), (1000, 1040), (300, 4112)])
+@pytest.mark.parametrize("N,K", [(17, 48), (100, 272), (1000, 1040), (90, 3072 + 16), (300, 4112)])
 def test_gemm_packed_equals_row_major_bitwise(M, N, K):
     rng = np.random.default_rng(M * 7919 + N * 31 + K + 1)
     a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)

@@ -67,10 +67,10 @@ def test_skinny_wide_weight_tiles(M):
 
 
 @pytest.mark.parametrize("M", [1, 2, 9, 40, 64])
-@pytest.mark.parametrize("K", [2048 + 16, 8192 + 128, 17408, 17408 + 16 * 7])
+@pytest.mark.parametrize("K", [2048 + 16, 3072 + 16, 3840, 8192 + 128, 17408, 17408 + 16 * 7])
 def test_skinny_long_k_splits(M, K):
-    """Long K: up to 4 waves per column tile (M <= 32) or up to 8 workgroup K-splits (M > 32), uneven
-    chunk counts, a partial last chunk."""
+    """Long K: 2, 3 or 4 waves per column tile (M <= 32; 9, 13, 15 and more chunks) or up to 8
+    workgroup K-splits (M > 32), uneven chunk counts, a partial last chunk."""
     rng = np.random.default_rng(K + M)
     N = 70 if M <= 32 else 200
     a, w = random_nvfp4(rng, M, K), random_nvfp4(rng, N, K)
