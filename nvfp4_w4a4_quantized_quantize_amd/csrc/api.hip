@@ -157,6 +157,10 @@ nvfp4_status gemm_entry(const uint8_t* a_codes, int64_t lda_c, const uint8_t* a_
     if (M < 0 || N < 0 || K < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
     if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K = %lld is not a multiple of 16", (long long)K);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return fail(NVFP4_ERR_SHAPE, "M or N too large");
+    // the tiled kernel's grid indices are 32-bit
+    if (M > nvfp4::SKINNY_MAX_M && ((M + 255) / 256) * ((N + 255) / 256) > (int64_t)1 << 30)
+        return fail(NVFP4_ERR_SHAPE, "M = %lld, N = %lld: more than 2^30 output tiles of 256 x 256", (long long)M,
+                    (long long)N);
     if (packed && M > nvfp4::SKINNY_MAX_M)
         return fail(NVFP4_ERR_SHAPE, "packed weights serve M <= %lld activation rows, M = %lld",
                     (long long)nvfp4::SKINNY_MAX_M, (long long)M);

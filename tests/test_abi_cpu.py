@@ -94,6 +94,7 @@ def g(L, M=8, N=64, K=64, segs=None, g_w=None, n_segs=None, g_a=1.0, a_codes=A16
     (dict(a_codes=None), 1), (dict(w_scales=None), 1),
     (dict(K=40), 2), (dict(M=-1), 2), (dict(lda_c=16), 2), (dict(ldw_s=0), 2),
     (dict(lda_c=1 << 23), 2), (dict(ldw_s=1 << 23), 2), (dict(M=300, ldw_c=1 << 23), 2),
+    (dict(M=1 << 31, N=1 << 30), 2),  # 2^23 x 2^22 output tiles: more than the tiled grid takes
     (dict(a_codes=A16 + 1), 3), (dict(lda_c=40), 3), (dict(ldw_s=24), 3),
     (dict(n_segs=0), 4), (dict(n_segs=17), 4),
     (dict(segs=[(0, 32, 0, 0, A16, 32, None, None)]), 4),
