@@ -67,6 +67,82 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+PEAK_GFX_MHZ = 2400.0  # MI355X peak engine clock, at which the matrix peak above is quoted
+
+
+def _gfx_mhz(amdsmi, dev):
+    """The graphics clock now (MHz): the mean over the XCDs from the GPU metrics table, else the
+    driver's current clock level; None when neither reads."""
+    try:
+        m = amdsmi.amdsmi_get_gpu_metrics_info(dev)
+        per_xcd = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, int) and 0 < v < 0xFFFF]
+        if per_xcd:
+            return float(np.mean(per_xcd))
+        v = m.get("current_gfxclk")
+        if isinstance(v, int) and 0 < v < 0xFFFF:
+            return float(v)
+    except Exception:  # noqa: BLE001 - a missing field or an unsupported query leaves the next source
+        pass
+    try:
+        v = amdsmi.amdsmi_get_clock_info(dev, amdsmi.AmdSmiClkType.GFX).get("clk")
+        return float(v) if isinstance(v, (int, float)) and v > 0 else None
+    except Exception:  # noqa: BLE001
+        return None
+
+
+def clock_under_load(fn, seconds: float = 2.0, period: float = 0.02) -> dict | None:
+    """Runs fn back to back for about `seconds` (untimed) while a thread reads the GPU metrics table
+    through amdsmi; returns the graphics clock (mean over the XCDs) and socket power over the second
+    half of the run, when the clock has settled under the load (the table refreshes about once a
+    second), or None when amdsmi cannot read them."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        devs = amdsmi.amdsmi_get_processor_handles()
+    except Exception:  # noqa: BLE001 - no amdsmi, or no access: the line reports no clock
+        return None
+    if len(devs) != 1:  # more than one GPU visible: which handle is cuda:0 is not known here
+        amdsmi.amdsmi_shut_down()
+        return None
+    samples, done = [], threading.Event()
+
+    def sample():
+        t_start = time.perf_counter()
+        while not done.is_set():
+            v = _gfx_mhz(amdsmi, devs[0])
+            try:
+                pw = amdsmi.amdsmi_get_gpu_metrics_info(devs[0]).get("current_socket_power")
+            except Exception:  # noqa: BLE001
+                pw = None
+            if v is not None:
+                samples.append((time.perf_counter() - t_start, v, pw if isinstance(pw, (int, float)) else None))
+            time.sleep(period)
+
+    th = threading.Thread(target=sample, daemon=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    done.set()
+    th.join()
+    amdsmi.amdsmi_shut_down()
+    late = [x for x in samples if x[0] >= seconds / 2]
+    if len(late) < 5:
+        return None
+    mhz = [x[1] for x in late]
+    pw = [x[2] for x in late if x[2] is not None]
+    return {"mean_mhz": float(np.mean(mhz)), "min_mhz": float(np.min(mhz)), "max_mhz": float(np.max(mhz)),
+            "socket_power_w": float(np.mean(pw)) if pw else None, "launches": n, "seconds": seconds,
+            "source": "amdsmi GPU metrics table (graphics clock, mean over the XCDs; refreshed about once a "
+                      "second), second half of a run of back-to-back launches"}
+
+
 def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
 
@@ -185,7 +261,9 @@ def run_gpu(step: Step, steps: int, warmup: int, flush_mb: int) -> dict:
     return {"wall_s": wall, "step_ms": step_ms, "quant_ms": float(np.mean(q_ms)), "quant_iso_ms": quant_iso_ms,
             "gemm_iso_ms": gemm_iso_ms,
             "gemm_ms": float(np.mean(g_ms)), "quant_ms_med": float(np.median(q_ms)),
-            "gemm_ms_med": float(np.median(g_ms))}
+            "gemm_ms_med": float(np.median(g_ms)),
+            "gemm_ms_p10_p90": [float(np.percentile(g_ms, 10)), float(np.percentile(g_ms, 90))],
+            "quant_ms_p10_p90": [float(np.percentile(q_ms, 10)), float(np.percentile(q_ms, 90))]}
 
 
 def time_quantizer_rotating(step: Step, copies: int = 3, reps: int = 10) -> dict:
@@ -269,6 +347,11 @@ def bench_other_configs(reps: int) -> dict:
         r = gemm_roofline(case, ms, packed)
         r.update({"workload": case.name + ("_packed" if packed else ""), "M": case.M, "N": case.N, "K": case.K,
                   "weight_copies": len(step.w_copies), "launches": n})
+        if r["roofline"]["bound"] == "mfma":
+            clk = clock_under_load(step.gemm, 1.5)
+            if clk is not None:
+                r["roofline"]["clock"] = clk
+                r["roofline"]["frac_at_clock"] = r["tflops"] / (PEAK_F16_MFMA_TFLOPS * clk["mean_mhz"] / PEAK_GFX_MHZ)
         res[key + ("_packed" if packed else "")] = r
         log(f"[gpu] {case.name}: {ms * 1e3:.1f} us, {r['tflops']:.1f} TFLOP/s, {r['gbps']:.0f} GB/s "
             f"({r['roofline']['bound']} {100 * r['roofline']['frac']:.1f}%)")
@@ -720,6 +803,17 @@ def main() -> int:
     roof.update({"traffic": tr[0] if tr else None, "traffic_detail": tr[1] if tr else None,
                  "kernel": kernel, "avg_ms": gemm_ms, "algorithmic_flop": flops,
                  "algorithmic_bytes": gemm_bytes})
+    # per-step event times of the timed steps (each GEMM interval also holds the event overhead)
+    roof["step_events_ms"] = {"gemm_median": r["gemm_ms_med"], "gemm_p10_p90": r["gemm_ms_p10_p90"],
+                              "quantize_median": r["quant_ms_med"], "quantize_p10_p90": r["quant_ms_p10_p90"]}
+    clk = clock_under_load(step.gemm)
+    if clk is not None:
+        roof["clock"] = clk
+        if mfma_bound:  # the matrix peak scales with the engine clock
+            roof["peak_at_clock"] = PEAK_F16_MFMA_TFLOPS * clk["mean_mhz"] / PEAK_GFX_MHZ
+            roof["frac_at_clock"] = gemm_tflops / roof["peak_at_clock"]
+        log(f"[gpu] graphics clock during the GEMM: {clk['mean_mhz']:.0f} MHz "
+            f"({clk['min_mhz']:.0f}-{clk['max_mhz']:.0f}), socket power {clk['socket_power_w']} W")
     trq = measured_traffic("quantize_kernel", f"x_{M}x{K}")
     copy_gbps = copy_ceiling_gbps()
     log(f"[gpu] plain device copy: {copy_gbps:.0f} GB/s (read + write)")
